@@ -1,0 +1,260 @@
+"""Benchmark of the KDA forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|varlen|long]
+
+A step is one pass of the prefill path over one batch of synthetic input resident
+in HBM: the conv4 + SiLU (+ q/k L2) prologue on q, k, v followed by the
+chunkwise KDA kernel (B=1, T=4096, H=96, dk=dv=128, chunk 64, bf16; final state
+written).  ``value`` is prefill tokens/s.  The same JSON line carries:
+
+* ``roofline``: the chunk kernel's algorithmic HBM bytes per launch divided by
+  its average launch duration, timed with HIP events on the stream it runs on,
+  against the 8 TB/s HBM peak; ``traffic`` is the measured HBM traffic per launch
+  from the committed rocprofv3 counter summary when it was taken on the current
+  kernel source, else null;
+* ``decode``: 256 in-place decode steps of 64 sequences x 96 heads (steps/s) and
+  the decode kernel's roofline;
+* ``cpu_baseline``: the fp64 oracle (prologue + recurrence) timed on this host's
+  cores on a bounded sample of heads of the same workload.
+
+Only one GPU is used; ``--gpus`` above 1 is refused.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "KDA prefill tokens/s (H=96, d=128) + decode steps/s; % of roofline"
+
+
+def kernel_source_digest() -> str:
+    """Hash of the sources the chunk kernel is built from (to date counter summaries)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "channel_gated_delta_amd", "csrc")
+    for name in ("kda_device.cuh", "kda_chunk.cuh", "kda_chunk_dispatch.cuh", "kda_chunk_bf16.hip"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch from profiles/<kind>_traffic.md if it matches the current source."""
+    path = os.path.join(ROOT, "profiles", "%s_traffic.md" % kind)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_digest:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_source_digest():
+        return None
+    return float(t.group(1))
+
+
+def prefill_step_bytes(T: int, H: int, dk: int, dv: int, N: int, h0: bool) -> float:
+    """Algorithmic HBM bytes of one chunk-kernel launch: every tensor once.
+
+    per token per head: q, k (bf16) 2*2*dk + v (bf16) 2*dv + g (fp32) 4*dk + beta 4
+    + o (bf16) 2*dv; plus the final state (and the initial state when given).
+    """
+    per_tok_head = 2 * dk + 2 * dk + 2 * dv + 4 * dk + 4 + 2 * dv
+    states = N * H * dk * dv * 4 * (2 if h0 else 1)
+    return float(T * H * per_tok_head + states)
+
+
+def prologue_bytes(T: int, H: int, d: int) -> float:
+    """conv4+SiLU(+L2): read x and write y (bf16) for q, k, v; weights are negligible."""
+    return float(3 * T * H * d * 2 * 2)
+
+
+def decode_step_bytes(B: int, H: int, dk: int, dv: int) -> float:
+    """State read + write (fp32) plus q, k, v, o (bf16), g (fp32), beta per (seq, head)."""
+    return float(B * H * (2 * dk * dv * 4 + 2 * dk * 2 + 2 * dv * 2 + 4 * dk + 4))
+
+
+def run_prefill(args, torch, kda, workloads):
+    specs = workloads.standard_specs()
+    spec = specs[args.workload]
+    dev = "cuda:0"
+    inp = workloads.make_prefill(spec, dev)
+    H, DK, DV = spec.heads, spec.dk, spec.dv
+    T, N = spec.total_tokens, len(spec.lengths)
+    cu = inp["cu_seqlens"] if N > 1 else None
+    qb = torch.empty((T, H, DK), dtype=spec.dtype, device=dev)
+    kb = torch.empty_like(qb)
+    vb = torch.empty((T, H, DV), dtype=spec.dtype, device=dev)
+    ob = torch.empty((T, H, DV), dtype=spec.dtype, device=dev)
+    hT = torch.empty((N, H, DK, DV), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        kda.short_conv(inp["q_raw"], inp["w_q"], num_heads=H, head_dim=DK, cu_seqlens=cu,
+                       l2_normalize=True, out=qb)
+        kda.short_conv(inp["k_raw"], inp["w_k"], num_heads=H, head_dim=DK, cu_seqlens=cu,
+                       l2_normalize=True, out=kb)
+        kda.short_conv(inp["v_raw"], inp["w_v"], num_heads=H, head_dim=DV, cu_seqlens=cu, out=vb)
+        if ev is not None:
+            ev[0].record(stream)
+        kda.chunk_fwd(qb, kb, vb, inp["g"], inp["beta"], cu_seqlens=cu, scale=spec.read_scale,
+                      gate_lower_bound=spec.gate_lb, chunk_size=spec.chunk,
+                      initial_state=inp["h0"], out=ob, final_state=hT)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(events[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    chunk_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
+    ms_step = total_ms / args.steps
+    return dict(spec=spec, T=T, N=N, ms_step=ms_step, chunk_ms=chunk_ms, inp=inp)
+
+
+def run_decode(torch, kda, workloads, steps=256, warmup=16):
+    spec = workloads.standard_specs()["decode"]
+    dev = "cuda:0"
+    B, H, DK, DV = spec.batch, spec.heads, spec.dk, spec.dv
+    state = workloads.make_decode_state(spec, dev)
+    ins = [workloads.make_decode_step(spec, t, dev) for t in range(steps)]
+    o = torch.empty((B, H, DV), dtype=spec.dtype, device=dev)
+    scratch = state.clone()
+    for t in range(warmup):
+        d = ins[t % steps]
+        kda.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], scratch, out=o)
+    del scratch
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for t in range(steps):
+        d = ins[t]
+        kda.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, out=o)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    return dict(spec=spec, steps=steps, ms=ms, B=B, H=H, DK=DK, DV=DV)
+
+
+def cpu_baseline(res, workloads):
+    """The oracle (fp64 prologue + recurrence) on a bounded sample of heads."""
+    import numpy as np
+    import oracle
+    spec, inp = res["spec"], res["inp"]
+    H, DK, DV = spec.heads, spec.dk, spec.dv
+    n_heads = max(1, min(H, int(os.environ.get("KDA_CPU_SAMPLE_HEADS", "24"))))
+    heads = list(range(n_heads))
+    f64 = lambda t: t.detach().double().cpu().numpy()  # noqa: E731
+
+    def chans(x, D):
+        return f64(x.view(x.shape[0], H, D)[:, heads, :].reshape(x.shape[0], n_heads * D))
+
+    def wch(w, D):
+        return f64(w.view(H, D, -1)[heads].reshape(n_heads * D, -1))
+
+    cu = inp["cu_seqlens"].cpu().numpy()
+    xq, xk, xv = chans(inp["q_raw"], DK), chans(inp["k_raw"], DK), chans(inp["v_raw"], DV)
+    wq, wk, wv = wch(inp["w_q"], DK), wch(inp["w_k"], DK), wch(inp["w_v"], DV)
+    g = f64(inp["g"][:, heads])
+    beta = f64(inp["beta"][:, heads])
+    h0 = None if inp["h0"] is None else f64(inp["h0"][:, heads])
+    oracle.default()
+    t0 = time.perf_counter()
+    q = oracle.prologue(xq, wq, n_heads, DK, cu, normalize=True)
+    k = oracle.prologue(xk, wk, n_heads, DK, cu, normalize=True)
+    v = oracle.prologue(xv, wv, n_heads, DV, cu)
+    oracle.recurrent(q, k, v, g, beta, cu, spec.read_scale, h0)
+    dt = time.perf_counter() - t0
+    # tokens/s of the whole workload: the sample covers n_heads of H heads
+    value = res["T"] / (dt * H / n_heads)
+    return {"value": value, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d heads x all %d tokens (fp64 conv+SiLU+L2 prologue and token-by-"
+                      "token recurrence), %.1f s wall, scaled by %d/%d" %
+                      (n_heads, H, res["T"], dt, H, n_heads)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "varlen", "long"])
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
+              "(no multi-GPU path exists)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import channel_gated_delta_amd as kda
+    from channel_gated_delta_amd import workloads
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if not os.path.exists(kda.LIB_PATH):
+        from channel_gated_delta_amd import build
+        build.build()
+    kda.library()
+
+    res = run_prefill(args, torch, kda, workloads)
+    spec = res["spec"]
+    H, DK, DV, T, N = spec.heads, spec.dk, spec.dv, res["T"], res["N"]
+    tok_s = T / (res["ms_step"] / 1e3)
+    alg_bytes = prefill_step_bytes(T, H, DK, DV, N, spec.h0_std is not None)
+    achieved = alg_bytes / (res["chunk_ms"] / 1e3) / 1e9
+    traffic = measured_traffic("chunk_%s" % args.workload)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "chunk_kernel (chunkwise KDA prefill)",
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "avg_launch_ms": round(res["chunk_ms"], 4)}
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; no weights or datasets)",
+        "config": {"workload": spec.name, "batch": N, "seq_len": T, "heads": H, "dk": DK,
+                   "dv": DV, "chunk": spec.chunk, "path": "3x short_conv (conv4+SiLU, q/k L2) + "
+                   "chunk_fwd"},
+        "roofline": roof,
+    }
+    if not args.no_decode:
+        d = run_decode(torch, kda, workloads)
+        ms_dec = d["ms"] / d["steps"]
+        dbytes = decode_step_bytes(d["B"], d["H"], d["DK"], d["DV"])
+        dach = dbytes / (ms_dec / 1e3) / 1e9
+        out["decode"] = {"value": round(d["steps"] / (d["ms"] / 1e3), 1), "unit": "steps/s",
+                         "workload": d["spec"].name, "ms_per_step": round(ms_dec, 4),
+                         "roofline": {"bound": "hbm", "achieved": round(dach, 1),
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": round(dach / HBM_PEAK_GBS, 4),
+                                      "traffic": measured_traffic("decode"),
+                                      "algorithmic_bytes_per_launch": dbytes}}
+    out["prologue_ms_per_step"] = round(res["ms_step"] - res["chunk_ms"], 4)
+    out["prologue_bytes_per_step"] = prologue_bytes(T, H, DK)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(res, workloads)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+"""KDA (Kimi Delta Attention) forward pass on AMD MI355X -- Python binding of libkda.
+
+Thin ctypes binding over the C ABI in include/kda.h.  It only checks and
+marshals arguments: every step of the computation runs in the HIP kernels of
+libkda.so.  PyTorch provides device memory and the current stream.  There is no
+fallback: if libkda.so is missing the calls raise.
+
+    short_conv(x, weight, ...)              -> (y, conv_state)   conv4 + SiLU (+ L2)
+    chunk_fwd(q, k, v, g, beta, ...)        -> (o, final_state)  chunkwise prefill
+    decode_step(q, k, v, g, beta, state)    -> o                 one recurrent step
+
+Build the library with ``python -m channel_gated_delta_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["KdaError", "library", "short_conv", "chunk_fwd", "decode_step", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+_lib = None
+_vp = ctypes.c_void_p
+_i32, _i64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("libkda status %d: %s" % (status, msg))
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """Load libkda.so (raises when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libkda.so is not built (%s); run `python -m "
+                               "channel_gated_delta_amd.build`" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.kda_short_conv.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp,
+                                       _i32, _i32, _f32, _i32, _vp, _vp]
+        lib.kda_chunk_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
+                                      _i32, _f32, _f32, _vp, _vp, _vp, _i32, _vp]
+        lib.kda_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
+                                        _vp, _i32, _vp]
+        for fn in ("kda_short_conv", "kda_chunk_fwd", "kda_decode_step"):
+            getattr(lib, fn).restype = ctypes.c_int
+        lib.kda_status_string.argtypes = [ctypes.c_int]
+        lib.kda_status_string.restype = ctypes.c_char_p
+        lib.kda_last_error.argtypes = []
+        lib.kda_last_error.restype = ctypes.c_char_p
+        lib.kda_version.argtypes = []
+        lib.kda_version.restype = ctypes.c_int32
+        _lib = lib
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != KDA_OK:
+        lib = library()
+        detail = lib.kda_last_error().decode() or lib.kda_status_string(status).decode()
+        raise KdaError(status, detail)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return t
+
+
+def _stream(t: torch.Tensor):
+    return _vp(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _seqs(cu_seqlens: Optional[torch.Tensor], total: int) -> int:
+    if cu_seqlens is None:
+        return 1
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be 1-D with num_seqs + 1 entries")
+    return cu_seqlens.numel() - 1
+
+
+def short_conv(x: torch.Tensor, weight: torch.Tensor, *, num_heads: int, head_dim: int,
+               cu_seqlens: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+               conv_state: Optional[torch.Tensor] = None, output_final_state: bool = False,
+               silu: bool = True, l2_normalize: bool = False, l2_eps: float = 1e-6,
+               out: Optional[torch.Tensor] = None, state_out: Optional[torch.Tensor] = None
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Causal depthwise conv (+SiLU, +per-head L2) over packed sequences.
+
+    x: [T, H*D]; weight: [H*D, W]; conv_state: [N, W-1, H*D] or None.
+    Returns y [T, H, D] and the new conv state [N, W-1, H*D] (if output_final_state
+    or ``state_out`` is given; ``state_out`` may be ``conv_state`` itself).
+    """
+    _dev(x, "x")
+    dt = x.dtype
+    if dt not in _DTYPES:
+        raise ValueError("x must be bf16 or fp32")
+    T = x.shape[0]
+    C = num_heads * head_dim
+    _dev(x, "x", dt, (T, C))
+    W = weight.shape[1] if weight.dim() == 2 else -1
+    _dev(weight, "weight", dt, (C, W))
+    if bias is not None:
+        _dev(bias, "bias", dt, (C,))
+    N = _seqs(cu_seqlens, T)
+    if conv_state is not None:
+        _dev(conv_state, "conv_state", dt, (N, W - 1, C))
+    y = out if out is not None else torch.empty((T, num_heads, head_dim), dtype=dt, device=x.device)
+    _dev(y, "out", dt, (T, num_heads, head_dim))
+    new_state = state_out
+    if new_state is None and output_final_state:
+        new_state = torch.empty((N, W - 1, C), dtype=dt, device=x.device)
+    if new_state is not None:
+        _dev(new_state, "state_out", dt, (N, W - 1, C))
+    _check(library().kda_short_conv(
+        _ptr(x), _ptr(weight), _ptr(bias), _ptr(cu_seqlens), N, T, num_heads, head_dim, W,
+        _ptr(conv_state), _ptr(new_state), 1 if silu else 0, 1 if l2_normalize else 0,
+        float(l2_eps), _DTYPES[dt], _ptr(y), _stream(x)))
+    return y, new_state
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+              beta: torch.Tensor, *, cu_seqlens: Optional[torch.Tensor] = None,
+              scale: Optional[float] = None, gate_lower_bound: float = -5.0, chunk_size: int = 64,
+              initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
+              out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA prefill.  q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H].
+
+    Returns o [T, H, dv] and the final states [N, H, dk, dv] (fp32) if requested.
+    """
+    _dev(q, "q")
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError("q must be bf16 or fp32")
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    _dev(k, "k", dt, (T, H, dk))
+    _dev(v, "v", dt, (T, H, dv))
+    _dev(g, "g", torch.float32, (T, H, dk))
+    _dev(beta, "beta", torch.float32, (T, H))
+    N = _seqs(cu_seqlens, T)
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", torch.float32, (N, H, dk, dv))
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _dev(final_state, "final_state", torch.float32, (N, H, dk, dv))
+    o = out if out is not None else torch.empty((T, H, dv), dtype=dt, device=q.device)
+    _dev(o, "out", dt, (T, H, dv))
+    sc = dk ** -0.5 if scale is None else float(scale)
+    _check(library().kda_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,
+        int(chunk_size), sc, float(gate_lower_bound), _ptr(initial_state), _ptr(final_state),
+        _ptr(o), _DTYPES[dt], _stream(q)))
+    return o, final_state
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                beta: torch.Tensor, state: torch.Tensor, *, scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One recurrent step; ``state`` [B, H, dk, dv] fp32 is updated in place.
+
+    q, k, g: [B, H, dk]; v: [B, H, dv]; beta: [B, H].  Returns o [B, H, dv].
+    """
+    _dev(q, "q")
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError("q must be bf16 or fp32")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    _dev(k, "k", dt, (B, H, dk))
+    _dev(v, "v", dt, (B, H, dv))
+    _dev(g, "g", torch.float32, (B, H, dk))
+    _dev(beta, "beta", torch.float32, (B, H))
+    _dev(state, "state", torch.float32, (B, H, dk, dv))
+    o = out if out is not None else torch.empty((B, H, dv), dtype=dt, device=q.device)
+    _dev(o, "out", dt, (B, H, dv))
+    sc = dk ** -0.5 if scale is None else float(scale)
+    _check(library().kda_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), B, H, dk, dv, sc, _ptr(o),
+        _DTYPES[dt], _stream(q)))
+    return o

@@ -1,0 +1,143 @@
+// kda_api.cpp -- the C ABI of libkda: host-side argument checks, then one or
+// two kernel launches on the caller's stream.  No allocation, no host sync.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "kda.h"
+#include "kda_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kda_status_t fail(kda_status_t st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+kda_status_t from_hip(hipError_t e, const char *what) {
+    if (e == hipSuccess) return KDA_OK;
+    if (e == hipErrorNotSupported) return fail(KDA_ERR_UNSUPPORTED, "%s: unsupported shape", what);
+    return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_dtype(kda_dtype_t d) { return d == KDA_DTYPE_F32 || d == KDA_DTYPE_BF16; }
+bool head_dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+int vec_elems(kda_dtype_t d) { return d == KDA_DTYPE_BF16 ? 8 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+KDA_API const char *kda_status_string(kda_status_t s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARG: return "invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "unsupported shape, dtype or gate bound";
+        case KDA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+KDA_API const char *kda_last_error(void) { return g_last_error; }
+
+KDA_API int32_t kda_version(void) { return 10000; }
+
+KDA_API kda_status_t kda_short_conv(const void *x, const void *weight, const void *bias,
+                                    const int32_t *cu_seqlens, int32_t num_seqs,
+                                    int64_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                    int32_t width, const void *conv_state_in, void *conv_state_out,
+                                    int32_t apply_silu, int32_t l2_normalize, float l2_eps,
+                                    kda_dtype_t dtype, void *y, void *stream) {
+    g_last_error[0] = '\0';
+    if (!weight || (total_tokens > 0 && (!x || !y)))
+        return fail(KDA_ERR_INVALID_ARG, "kda_short_conv: NULL x/weight/y");
+    if (num_seqs < 1 || total_tokens < 0 || num_heads < 1 || head_dim < 1)
+        return fail(KDA_ERR_INVALID_ARG, "kda_short_conv: bad sizes");
+    if (!cu_seqlens && num_seqs != 1)
+        return fail(KDA_ERR_INVALID_ARG, "kda_short_conv: cu_seqlens NULL needs num_seqs == 1");
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "kda_short_conv: bad dtype");
+    if (x && x == y) return fail(KDA_ERR_INVALID_ARG, "kda_short_conv: y aliases x");
+    if (l2_normalize && !(l2_eps >= 0.f && isfinite(l2_eps)))
+        return fail(KDA_ERR_INVALID_ARG, "kda_short_conv: l2_eps must be finite and >= 0");
+    if (width < 1 || width > 4) return fail(KDA_ERR_UNSUPPORTED, "kda_short_conv: width not in 1..4");
+    const int ve = vec_elems(dtype);
+    if (head_dim % ve != 0)
+        return fail(KDA_ERR_UNSUPPORTED, "kda_short_conv: head_dim not a multiple of %d", ve);
+    if (l2_normalize) {
+        const int lanes = head_dim / ve;
+        if (lanes > 64 || (lanes & (lanes - 1)) != 0)
+            return fail(KDA_ERR_UNSUPPORTED, "kda_short_conv: head_dim/%d must be a power of two <= 64", ve);
+    }
+    if ((int64_t)num_heads * head_dim > (int64_t)1 << 30 || total_tokens > ((int64_t)1 << 40))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_short_conv: size too large");
+    kda::ConvArgs a{x, weight, bias, cu_seqlens, num_seqs, total_tokens, num_heads, head_dim,
+                    width, conv_state_in, conv_state_out, apply_silu, l2_normalize, l2_eps, y};
+    return from_hip(kda::launch_short_conv(a, dtype == KDA_DTYPE_BF16, (hipStream_t)stream),
+                    "kda_short_conv");
+}
+
+KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                                   const float *beta, const int32_t *cu_seqlens, int32_t num_seqs,
+                                   int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                                   int32_t chunk_size, float scale, float gate_lower_bound,
+                                   const float *initial_state, float *final_state, void *o,
+                                   kda_dtype_t dtype, void *stream) {
+    g_last_error[0] = '\0';
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o))
+        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: NULL q/k/v/g/beta/o");
+    if (num_seqs < 1 || total_tokens < 0 || num_heads < 1)
+        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: bad sizes");
+    if (!cu_seqlens && num_seqs != 1)
+        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: cu_seqlens NULL needs num_seqs == 1");
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: bad dtype");
+    if (!isfinite(scale)) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: scale not finite");
+    if (o && (o == q || o == k || o == v || o == (const void *)g || o == (const void *)beta))
+        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: o aliases an input");
+    if (!(gate_lower_bound <= 0.f)) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: gate bound > 0 or NaN");
+    if (gate_lower_bound < -10.f)
+        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: gate_lower_bound below -10");
+    if (!head_dim_ok(dk) || !head_dim_ok(dv))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: dk/dv not in {16,32,64,128}");
+    if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: chunk_size not in {16,32,64}");
+    if ((int64_t)num_seqs * num_heads * (dv / 16) > ((int64_t)1 << 28))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: grid too large");
+    kda::ChunkArgs a{q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, dk, dv,
+                     chunk_size, scale, gate_lower_bound, initial_state, final_state, o};
+    const bool bf = dtype == KDA_DTYPE_BF16;
+    bool ok = false;
+    (void)(bf ? kda::launch_chunk_bf16 : kda::launch_chunk_f32)(a, (hipStream_t)stream, false, &ok);
+    if (!ok) return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: no kernel for dk=%d dv=%d", dk, dv);
+    return from_hip((bf ? kda::launch_chunk_bf16 : kda::launch_chunk_f32)(a, (hipStream_t)stream,
+                                                                           true, &ok),
+                    "kda_chunk_fwd");
+}
+
+KDA_API kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const float *g,
+                                     const float *beta, float *state, int32_t batch,
+                                     int32_t num_heads, int32_t dk, int32_t dv, float scale,
+                                     void *o, kda_dtype_t dtype, void *stream) {
+    g_last_error[0] = '\0';
+    if (batch > 0 && (!q || !k || !v || !g || !beta || !state || !o))
+        return fail(KDA_ERR_INVALID_ARG, "kda_decode_step: NULL pointer");
+    if (batch < 0 || num_heads < 1) return fail(KDA_ERR_INVALID_ARG, "kda_decode_step: bad sizes");
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "kda_decode_step: bad dtype");
+    if (!isfinite(scale)) return fail(KDA_ERR_INVALID_ARG, "kda_decode_step: scale not finite");
+    if (o && (o == q || o == k || o == v || o == (const void *)g || o == (const void *)beta ||
+              o == (const void *)state))
+        return fail(KDA_ERR_INVALID_ARG, "kda_decode_step: o aliases an input");
+    if (!head_dim_ok(dk) || !head_dim_ok(dv))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: dk/dv not in {16,32,64,128}");
+    if ((int64_t)batch * num_heads > ((int64_t)1 << 31) - 1)
+        return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: grid too large");
+    kda::DecodeArgs a{q, k, v, g, beta, state, batch, num_heads, dk, dv, scale, o};
+    return from_hip(kda::launch_decode_step(a, dtype == KDA_DTYPE_BF16, (hipStream_t)stream),
+                    "kda_decode_step");
+}
+
+}  // extern "C"

@@ -1,0 +1,8 @@
+// fp32 instantiations of the chunkwise prefill kernel (fp32 MFMA throughout).
+#include "kda_chunk_dispatch.cuh"
+
+namespace kda {
+hipError_t launch_chunk_f32(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok) {
+    return chunk_detail::dispatch<float>(a, s, launch, ok);
+}
+}  // namespace kda

@@ -1,0 +1,102 @@
+// kda_device.cuh -- device-side building blocks shared by the KDA kernels:
+// element types, vector loads, wave reductions and 16x16 MFMA tile fragments
+// for CDNA4 (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+// One 16-byte vector of T (8 bf16 or 4 fp32).
+template <class T> struct Vec16;
+template <> struct Vec16<bf16> { static constexpr int n = 8; typedef bf16x8 type; };
+template <> struct Vec16<float> { static constexpr int n = 4; typedef f32x4 type; };
+
+template <class T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// 2^x on the transcendental unit (v_exp_f32); the argument is clamped so the
+// result stays finite (2^126 < FLT_MAX).
+__device__ __forceinline__ float exp2_clamped(float x) {
+    return __builtin_amdgcn_exp2f(fminf(x, 126.0f));
+}
+
+// Sum over groups of `width` consecutive lanes (width a power of two <= 64).
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int off = width / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, width);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// 16x16 MFMA tiles.
+//
+// A tile product D(16x16) += A(16xK) * B(Kx16) is issued in K-steps of
+// 4*KPL: lane l supplies row (l & 15) of A and column (l & 15) of B, each with
+// the KPL consecutive k indices starting at (l >> 4) * KPL.  Both operands are
+// read from LDS matrices stored with k contiguous: A as [rows][K] and B as
+// [cols][K] (i.e. B transposed).  The accumulator holds D[(l >> 4) * 4 + r][l & 15]
+// in element r.
+//
+// KPL = 8 (bf16): v_mfma_f32_16x16x32_bf16;  KPL = 4 (bf16): ..._16x16x16_bf16;
+// KPL = 1 (fp32): v_mfma_f32_16x16x4_f32.
+// ---------------------------------------------------------------------------
+template <class T, int KPL> struct Frag;
+template <> struct Frag<bf16, 8> { typedef bf16x8 type; };
+template <> struct Frag<bf16, 4> { typedef bf16x4 type; };
+template <> struct Frag<float, 1> { typedef float type; };
+
+template <class T, int KPL>
+__device__ __forceinline__ typename Frag<T, KPL>::type load_frag(const T *base, int ld, int row0,
+                                                                 int k0, int lane) {
+    const T *p = base + (row0 + (lane & 15)) * ld + k0 + (lane >> 4) * KPL;
+    return *reinterpret_cast<const typename Frag<T, KPL>::type *>(p);
+}
+
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// k per lane for a product whose reduction length is K.
+template <class T, int K> struct KplFor { static constexpr int value = 1; };
+template <int K> struct KplFor<bf16, K> { static constexpr int value = (K % 32 == 0) ? 8 : 4; };
+
+// D += A[arow0.., kbeg..kend) * B[brow0.., kbeg..kend)^T with A, B k-contiguous in LDS.
+// kbeg/kend must be multiples of the K-step 4*KPL.
+template <class T, int KPL>
+__device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const T *A, int lda, int arow0, const T *B,
+                                          int ldb, int brow0, int kbeg, int kend, int lane) {
+    for (int k0 = kbeg; k0 < kend; k0 += 4 * KPL) {
+        auto a = load_frag<T, KPL>(A, lda, arow0, k0, lane);
+        auto b = load_frag<T, KPL>(B, ldb, brow0, k0, lane);
+        acc = mma(a, b, acc);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ int acc_row(int lane, int r) { return (lane >> 4) * 4 + r; }
+__device__ __forceinline__ int acc_col(int lane) { return lane & 15; }
+
+}  // namespace kda

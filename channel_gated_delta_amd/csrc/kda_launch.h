@@ -1,0 +1,52 @@
+// kda_launch.h -- internal launchers behind the C ABI (host code; not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct ConvArgs {
+    const void *x, *weight, *bias;
+    const int32_t *cu_seqlens;
+    int32_t num_seqs;
+    int64_t total_tokens;
+    int32_t heads, head_dim, width;
+    const void *state_in;
+    void *state_out;
+    int32_t silu, l2;
+    float eps;
+    void *y;
+};
+
+struct ChunkArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const int32_t *cu_seqlens;
+    int32_t num_seqs;
+    int64_t total_tokens;
+    int32_t heads, dk, dv, chunk;
+    float scale, gate_lb;
+    const float *h0;
+    float *hT;
+    void *o;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float *state;
+    int32_t batch, heads, dk, dv;
+    float scale;
+    void *o;
+};
+
+// Each launcher returns hipSuccess, hipErrorNotSupported for a shape it has no
+// kernel for (checked before anything is enqueued), or the launch error.
+hipError_t launch_short_conv(const ConvArgs &a, bool bf16, hipStream_t s);
+// Chunk prefill per dtype: with launch == false only *ok (shape supported) is set.
+hipError_t launch_chunk_bf16(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok);
+hipError_t launch_chunk_f32(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok);
+hipError_t launch_decode_step(const DecodeArgs &a, bool bf16, hipStream_t s);
+
+}  // namespace kda

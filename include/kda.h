@@ -1,0 +1,177 @@
+/*
+ * kda.h -- C ABI of libkda, the Kimi Delta Attention (KDA) forward pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [Walkthrough]   "Kimi K3的线性注意力：从源码看懂KDA如何更新记忆"
+ *   [Replication-2] "KimiK3轻量化复刻实现KDA并行解析，Chunkwise并行与状态压缩机制详解"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every tensor pointer is DEVICE memory owned by the caller, dense,
+ *           row-major and contiguous, aligned to at least 16 bytes.  The library
+ *           allocates nothing, keeps no global mutable state and never
+ *           synchronises the host with the device.
+ * Streams.  Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *           and is asynchronous: outputs are valid once that stream has reached
+ *           the enqueued work.
+ * Packing.  Variable-length batches are packed along the token axis; cu_seqlens
+ *           is an int32 DEVICE array of num_seqs+1 non-decreasing offsets with
+ *           cu_seqlens[0] = 0 and cu_seqlens[num_seqs] = total_tokens.  NULL means
+ *           one sequence of total_tokens tokens (num_seqs must then be 1).  Its
+ *           contents cannot be checked on the host without a sync; offsets
+ *           outside [0, total_tokens] are clamped by the kernels, so a malformed
+ *           array yields unspecified values but no out-of-bounds access.
+ * Dtypes.   `dtype` names the activation dtype (q, k, v, o, conv input/output,
+ *           conv weights and conv state).  Gates (g, beta) and recurrent states
+ *           are always fp32.  bf16 results are rounded to nearest even.
+ * Empty.    With zero tokens (batch 0 for decode) the activation pointers may be
+ *           NULL; states are still copied/produced as documented.
+ * Errors.   Every call returns a kda_status_t.  Argument checks run on the host
+ *           before anything is enqueued; a failed check enqueues nothing and
+ *           leaves every output untouched.  KDA_ERR_HIP reports a launch failure
+ *           (kda_last_error() gives the HIP message).  Nothing throws across the
+ *           ABI.  The calls are thread-safe and re-entrant across streams.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef KDA_API
+#define KDA_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* NULL required pointer, negative size, inconsistent sizes */
+    KDA_ERR_UNSUPPORTED = 2, /* valid but not implemented shape / dtype / gate bound */
+    KDA_ERR_HIP = 3          /* the HIP runtime rejected a launch */
+} kda_status_t;
+
+typedef enum {
+    KDA_DTYPE_F32 = 0,
+    KDA_DTYPE_BF16 = 1
+} kda_dtype_t;
+
+/*
+ * kda_short_conv -- causal depthwise convolution + SiLU, optionally followed by
+ * a per-head L2 normalisation (the q/k/v prologue of the KDA layer).
+ *
+ * Defined by [Walkthrough] 第二站 (each of q, k, v passes a width-4 causal conv
+ * that mixes the current position with up to three earlier ones, SiLU lives in
+ * the conv module, a conv cache carries the history between calls, packed
+ * sequences are passed by cu_seqlens; q and k are then L2-normalised inside the
+ * KDA operator) and [Replication-2] (per-channel width-4 causal Conv1D).
+ *
+ * For sequence n and channel c (C = num_heads * head_dim channels), with history
+ * h_0..h_{W-2} (oldest first) = conv_state_in[n, :, c] or zeros, the j-th token
+ * of the sequence gets
+ *     y = bias[c] + sum_{i=0}^{W-1} weight[c, i] * xe[j + i],
+ *     xe = [h_0, .., h_{W-2}, x_bos, .., x_{eos-1}]
+ * (weight[c, W-1] multiplies the current token), then y <- y * sigmoid(y) if
+ * apply_silu, then, if l2_normalize, every group of head_dim channels of a
+ * token is scaled by 1 / sqrt(sum y^2 + l2_eps).  The history restarts at every
+ * sequence start.
+ *
+ *   x              [total_tokens, num_heads * head_dim]   dtype
+ *   weight         [num_heads * head_dim, width]           dtype
+ *   bias           [num_heads * head_dim] dtype, or NULL
+ *   conv_state_in  [num_seqs, width-1, num_heads*head_dim] dtype, or NULL (zeros)
+ *   conv_state_out same shape, or NULL; receives the last width-1 inputs of each
+ *                  sequence (history included when the sequence is shorter).
+ *                  May alias conv_state_in.
+ *   y              [total_tokens, num_heads, head_dim]     dtype; must not alias x.
+ * Supported: width in 1..4; head_dim a multiple of the 16-byte vector (8 bf16 /
+ * 4 fp32); with l2_normalize, head_dim / vector must be a power of two <= 64
+ * (head_dim <= 512 bf16 / 256 fp32); total_tokens >= 0 (0 enqueues only the
+ * state copy).
+ */
+KDA_API kda_status_t kda_short_conv(const void *x, const void *weight, const void *bias,
+                            const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                            int32_t num_heads, int32_t head_dim, int32_t width,
+                            const void *conv_state_in, void *conv_state_out,
+                            int32_t apply_silu, int32_t l2_normalize, float l2_eps,
+                            kda_dtype_t dtype, void *y, void *stream);
+
+/*
+ * kda_chunk_fwd -- chunkwise-parallel KDA prefill over packed sequences.
+ *
+ * Computes exactly the token-by-token recurrence of [Walkthrough] 第三站-第五站:
+ * for each (sequence n, head h), S <- initial_state[n,h] (or zeros) and per token
+ *     S <- diag(exp(g_t)) S;  e = v_t - S^T k_t;  S <- S + beta_t k_t e^T;
+ *     o_t = scale * S^T q_t,
+ * and final_state[n,h] = S after the sequence.  The work is organised in chunks
+ * of chunk_size tokens that pass the state from chunk to chunk while the work
+ * inside a chunk runs as matrix products ([Walkthrough] 彩蛋; [Replication-2]
+ * 图1); chunks restart at every sequence start and the last one may be partial.
+ * The result does not depend on chunk_size beyond rounding.
+ *
+ *   q, k           [total_tokens, num_heads, dk]   dtype (q, k usually unit length)
+ *   v              [total_tokens, num_heads, dv]   dtype
+ *   g              [total_tokens, num_heads, dk]   fp32 log-decay, gate_lower_bound <= g <= 0
+ *   beta           [total_tokens, num_heads]       fp32
+ *   initial_state  [num_seqs, num_heads, dk, dv]   fp32 (key index first), or NULL = zeros
+ *   final_state    [num_seqs, num_heads, dk, dv]   fp32, or NULL = not written;
+ *                  may alias initial_state.
+ *   o              [total_tokens, num_heads, dv]   dtype; must not alias any input.
+ * scale is the read-out scale (the pages leave the query scale to the caller;
+ * dk^-1/2 is the usual choice).  gate_lower_bound is the floor of g promised by
+ * the caller ([Walkthrough] 彩蛋: the bounded gate keeps sub-chunk decay products
+ * inside the floating-point range); it must be in [-10, 0].  g below the
+ * promised floor gives unspecified accuracy but no out-of-bounds access.
+ * Supported: dk, dv in {16, 32, 64, 128}; chunk_size in {16, 32, 64};
+ * |q|, |k| entries below 1e3.  The fp32 dtype computes in fp32 throughout; the
+ * bf16 dtype runs its products on bf16 matrix cores with fp32 accumulation and
+ * keeps the recurrent state in fp32.  When a shape's working set does not fit
+ * in a CU's 160 KiB LDS at the requested chunk_size (fp32 with dk = 128), the
+ * kernel runs the next smaller chunk size instead.
+ */
+KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const int32_t *cu_seqlens, int32_t num_seqs,
+                           int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                           int32_t chunk_size, float scale, float gate_lower_bound,
+                           const float *initial_state, float *final_state, void *o,
+                           kda_dtype_t dtype, void *stream);
+
+/*
+ * kda_decode_step -- one recurrent KDA step for a batch of sequences, updating
+ * the fp32 states in place (token-by-token execution for generation,
+ * [Walkthrough] 彩蛋; update order of 第三站-第五站).
+ *
+ * For each (b, h): S <- diag(exp(g)) S; e = v - S^T k; S <- S + beta k e^T;
+ * o = scale * S^T q.  Inputs are already conv-processed and q, k normalised;
+ * the step does no convolution and no normalisation.
+ *
+ *   q, k   [batch, num_heads, dk]        dtype
+ *   v      [batch, num_heads, dv]        dtype
+ *   g      [batch, num_heads, dk]        fp32 log-decay
+ *   beta   [batch, num_heads]            fp32
+ *   state  [batch, num_heads, dk, dv]    fp32, read and written IN PLACE
+ *   o      [batch, num_heads, dv]        dtype; must not alias any input.
+ * Supported: dk, dv in {16, 32, 64, 128}.
+ */
+KDA_API kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, float *state, int32_t batch, int32_t num_heads,
+                             int32_t dk, int32_t dv, float scale, void *o, kda_dtype_t dtype,
+                             void *stream);
+
+/* Static description of a status code (never NULL). */
+KDA_API const char *kda_status_string(kda_status_t status);
+
+/* Detail of the last failed call on the calling thread ("" if none). */
+KDA_API const char *kda_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+KDA_API int32_t kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

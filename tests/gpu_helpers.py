@@ -1,0 +1,83 @@
+"""Shared plumbing of the GPU parity tests: run the HIP path through the binding,
+run the oracle on the same inputs (optionally on a sample of heads), compare."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import channel_gated_delta_amd as kda
+import oracle
+from channel_gated_delta_amd import workloads
+
+TOL_BF16 = 2e-2   # max|gpu - oracle| / rms(oracle), bf16 inputs
+TOL_F32 = 1e-4    # same, fp32 inputs
+
+
+def tol_for(dtype) -> float:
+    return TOL_BF16 if dtype == torch.bfloat16 else TOL_F32
+
+
+def note(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().double().cpu().numpy()
+
+
+def gpu_prefill(inp, spec, chunk=None, out=None):
+    """HIP path: prologue (if the workload has raw projections) then chunk_fwd."""
+    H, DK, DV = spec.heads, spec.dk, spec.dv
+    cu = inp["cu_seqlens"]
+    if spec.conv:
+        q, _ = kda.short_conv(inp["q_raw"], inp["w_q"], num_heads=H, head_dim=DK, cu_seqlens=cu,
+                              l2_normalize=True)
+        k, _ = kda.short_conv(inp["k_raw"], inp["w_k"], num_heads=H, head_dim=DK, cu_seqlens=cu,
+                              l2_normalize=True)
+        v, _ = kda.short_conv(inp["v_raw"], inp["w_v"], num_heads=H, head_dim=DV, cu_seqlens=cu)
+    else:
+        q, k, v = inp["q"], inp["k"], inp["v"]
+    o, hT = kda.chunk_fwd(q, k, v, inp["g"], inp["beta"], cu_seqlens=cu, scale=spec.read_scale,
+                          gate_lower_bound=spec.gate_lb, chunk_size=chunk or spec.chunk,
+                          initial_state=inp["h0"], out=out)
+    return dict(q=q, k=k, v=v, o=o, hT=hT)
+
+
+def oracle_prefill(inp, spec, heads):
+    """Oracle on the sampled heads: fp64 prologue (conv + SiLU + L2) and recurrence."""
+    H, DK, DV = spec.heads, spec.dk, spec.dv
+    cu = inp["cu_seqlens"].cpu().numpy()
+    heads = list(heads)
+
+    def chans(x, D):
+        x = x.view(x.shape[0], H, D)[:, heads, :]
+        return to64(x.reshape(x.shape[0], len(heads) * D))
+
+    def wch(w, D):
+        return to64(w.view(H, D, -1)[heads].reshape(len(heads) * D, -1))
+
+    if spec.conv:
+        q = oracle.prologue(chans(inp["q_raw"], DK), wch(inp["w_q"], DK), len(heads), DK, cu,
+                            normalize=True)
+        k = oracle.prologue(chans(inp["k_raw"], DK), wch(inp["w_k"], DK), len(heads), DK, cu,
+                            normalize=True)
+        v = oracle.prologue(chans(inp["v_raw"], DV), wch(inp["w_v"], DV), len(heads), DV, cu)
+    else:
+        q = to64(inp["q"][:, heads])
+        k = to64(inp["k"][:, heads])
+        v = to64(inp["v"][:, heads])
+    g = to64(inp["g"][:, heads])
+    beta = to64(inp["beta"][:, heads])
+    h0 = None if inp["h0"] is None else to64(inp["h0"][:, heads])
+    o, hT = oracle.recurrent(q, k, v, g, beta, cu_seqlens=cu, scale=spec.read_scale, h0=h0)
+    return dict(q=q, k=k, v=v, o=o, hT=hT)
+
+
+def assert_parity(name, got, ref, tol):
+    err = oracle.rel_err(got, ref)
+    note("  %-28s rel err %.3e (tol %.0e)" % (name, err, tol))
+    assert np.isfinite(err) and err <= tol, "%s: rel err %.3e > %.0e" % (name, err, tol)
+    return err

@@ -1,0 +1,130 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/kda.h, and rejects bad arguments on the host before
+anything is enqueued (fake non-NULL pointers are never dereferenced there)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import channel_gated_delta_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+P = ctypes.c_void_p(4096)   # stand-in device pointer: only compared, never dereferenced
+NULL = None
+BF16, F32 = 1, 0
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"KDA_API\s+[\w\s\*]+?\b(kda_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        from channel_gated_delta_amd import build
+        build.build(verbose=False)
+    return kda.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == {"kda_short_conv", "kda_chunk_fwd", "kda_decode_step",
+                          "kda_status_string", "kda_last_error", "kda_version"}
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_only_the_abi_is_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == set(declared_functions())
+
+
+def test_status_strings_and_version(lib):
+    for st in range(4):
+        assert lib.kda_status_string(st)
+    assert lib.kda_status_string(99) == b"unknown status"
+    assert lib.kda_version() >= 10000
+
+
+def chunk(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, cu=NULL, N=1, T=64, H=2, dk=128, dv=128, chunk=64,
+             scale=0.1, lb=-5.0, h0=NULL, hT=NULL, o=ctypes.c_void_p(8192), dtype=BF16)
+    a.update(kw)
+    return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"], a["T"],
+                             a["H"], a["dk"], a["dv"], a["chunk"], a["scale"], a["lb"], a["h0"],
+                             a["hT"], a["o"], a["dtype"], NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), kda.KDA_ERR_INVALID_ARG),
+    (dict(o=NULL), kda.KDA_ERR_INVALID_ARG),
+    (dict(N=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(N=2), kda.KDA_ERR_INVALID_ARG),            # cu_seqlens NULL with two sequences
+    (dict(T=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(H=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(dtype=7), kda.KDA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), kda.KDA_ERR_INVALID_ARG),
+    (dict(o=P), kda.KDA_ERR_INVALID_ARG),            # o aliases q
+    (dict(lb=0.5), kda.KDA_ERR_INVALID_ARG),
+    (dict(lb=float("nan")), kda.KDA_ERR_INVALID_ARG),
+    (dict(lb=-11.0), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dk=48), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dv=256), kda.KDA_ERR_UNSUPPORTED),
+    (dict(chunk=128), kda.KDA_ERR_UNSUPPORTED),
+    (dict(chunk=8), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_chunk_fwd_rejects(lib, kw, status):
+    assert chunk(lib, **kw) == status
+    assert lib.kda_last_error()
+
+
+def conv(lib, **kw):
+    a = dict(x=P, w=P, b=NULL, cu=NULL, N=1, T=16, H=2, D=128, W=4, sin=NULL, sout=NULL, silu=1,
+             l2=1, eps=1e-6, dtype=BF16, y=ctypes.c_void_p(8192))
+    a.update(kw)
+    return lib.kda_short_conv(a["x"], a["w"], a["b"], a["cu"], a["N"], a["T"], a["H"], a["D"],
+                              a["W"], a["sin"], a["sout"], a["silu"], a["l2"], a["eps"],
+                              a["dtype"], a["y"], NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=NULL), kda.KDA_ERR_INVALID_ARG),
+    (dict(y=P), kda.KDA_ERR_INVALID_ARG),            # y aliases x
+    (dict(N=3), kda.KDA_ERR_INVALID_ARG),
+    (dict(T=-5), kda.KDA_ERR_INVALID_ARG),
+    (dict(eps=-1.0), kda.KDA_ERR_INVALID_ARG),
+    (dict(W=5), kda.KDA_ERR_UNSUPPORTED),
+    (dict(W=0), kda.KDA_ERR_UNSUPPORTED),
+    (dict(D=12), kda.KDA_ERR_UNSUPPORTED),           # not a multiple of 8 bf16
+    (dict(D=24), kda.KDA_ERR_UNSUPPORTED),           # 3 vectors per head: not a power of two
+    (dict(D=1024), kda.KDA_ERR_UNSUPPORTED),         # 128 vectors per head
+])
+def test_short_conv_rejects(lib, kw, status):
+    assert conv(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(state=NULL), kda.KDA_ERR_INVALID_ARG),
+    (dict(B=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(o=P), kda.KDA_ERR_INVALID_ARG),
+    (dict(dk=8), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_decode_step_rejects(lib, kw, status):
+    a = dict(state=ctypes.c_void_p(12288), B=4, H=2, dk=128, dv=128, o=ctypes.c_void_p(8192))
+    a.update(kw)
+    assert lib.kda_decode_step(P, P, P, P, P, a["state"], a["B"], a["H"], a["dk"], a["dv"], 0.1,
+                               a["o"], BF16, NULL) == status
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 2, 16)
+    with pytest.raises(ValueError):
+        kda.chunk_fwd(x, x, x, x, x[..., 0])

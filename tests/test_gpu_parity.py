@@ -1,0 +1,241 @@
+"""HIP path vs the fp64 oracle, element by element, on seeded inputs (needs an MI355X).
+
+Sizes the oracle finishes in seconds, spanning several 16-token tiles, several
+chunks and ragged tails, plus edge cases; the full workload shapes live in
+test_gpu_workloads.py.  Bar: max|gpu - oracle| / rms(oracle) <= 2e-2 for bf16
+inputs and <= 1e-4 for fp32 inputs (outputs and final states); the prologue is
+held to one rounding of its output dtype, element by element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import channel_gated_delta_amd as kda
+import oracle
+from channel_gated_delta_amd import workloads
+from gpu_helpers import (assert_parity, gpu_prefill, note, oracle_prefill, to64, tol_for)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+RAGGED = [1, 3, 15, 17, 63, 65, 130]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    kda.library()
+
+
+def spec_of(lengths, H=3, dk=128, dv=128, chunk=64, dtype=torch.bfloat16, conv=False, lb=-5.0,
+            gate_std=1.0, h0=None, seed=0):
+    return workloads.PrefillSpec("t", list(lengths), heads=H, dk=dk, dv=dv, chunk=chunk,
+                                 dtype=dtype, conv=conv, gate_lb=lb, gate_std=gate_std,
+                                 h0_std=h0, seed=seed)
+
+
+def check_prefill(spec, heads=None, chunk=None):
+    inp = workloads.make_prefill(spec, DEV)
+    got = gpu_prefill(inp, spec, chunk=chunk)
+    torch.cuda.synchronize()
+    heads = list(range(spec.heads)) if heads is None else list(heads)
+    ref = oracle_prefill(inp, spec, heads)
+    tol = tol_for(spec.dtype)
+    assert_parity("o", to64(got["o"][:, heads]), ref["o"], tol)
+    assert_parity("final state", to64(got["hT"][:, heads]), ref["hT"], tol)
+    return inp, got, ref
+
+
+def test_tiny_fp32_workload():
+    """B=1, H=1, T=64, d=16, chunk 16, fp32, q/k unit length, scale 1: tolerance 1e-4."""
+    check_prefill(workloads.standard_specs()["tiny_fp32"])
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_ragged_varlen_with_h0(chunk, dtype):
+    note("ragged varlen %s chunk=%d" % (dtype, chunk))
+    check_prefill(spec_of(RAGGED, H=2, chunk=chunk, dtype=dtype, h0=0.05, seed=chunk))
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (64, 64), (128, 16), (16, 128)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_head_dims(dk, dv, dtype):
+    note("dims dk=%d dv=%d %s" % (dk, dv, dtype))
+    check_prefill(spec_of([200, 37], H=3, dk=dk, dv=dv, dtype=dtype, h0=0.1, seed=dk + dv))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_prologue_pipeline_varlen(dtype):
+    """conv + SiLU + L2 prologue feeding the chunk kernel, several sequences."""
+    check_prefill(spec_of([300, 5, 129, 64], H=4, dtype=dtype, conv=True, h0=0.05, seed=11))
+
+
+@pytest.mark.parametrize("lb,std", [(-8.0, 2.0), (-10.0, 3.0)])
+def test_strong_decay(lb, std):
+    """Gate floors below -5 (16-token decay span up to e^-160): finite and accurate."""
+    check_prefill(spec_of([256, 77], H=2, lb=lb, gate_std=std, h0=0.05, seed=int(-lb)))
+
+
+def test_identity_gate_keeps_state():
+    """g = 0, beta = 0: the final state equals h0 and o = scale * S0^T q."""
+    spec = spec_of([96, 40], H=2, h0=0.1, seed=5)
+    inp = workloads.make_prefill(spec, DEV)
+    inp["g"].zero_()
+    inp["beta"].zero_()
+    got = gpu_prefill(inp, spec)
+    torch.cuda.synchronize()
+    assert torch.equal(got["hT"], inp["h0"])
+    ref = oracle_prefill(inp, spec, [0, 1])
+    assert_parity("o", to64(got["o"]), ref["o"], 2e-2)
+
+
+def test_empty_and_single_token_sequences():
+    spec = spec_of([0, 1, 0, 70, 0], H=2, h0=0.05, seed=6)
+    check_prefill(spec)
+
+
+def test_zero_tokens():
+    spec = spec_of([0], H=2, h0=0.05, seed=7)
+    inp = workloads.make_prefill(spec, DEV)
+    got = gpu_prefill(inp, spec)
+    torch.cuda.synchronize()
+    assert got["o"].numel() == 0
+    assert torch.equal(got["hT"], inp["h0"])
+
+
+def test_chunk_sizes_agree_and_deterministic():
+    spec = spec_of([333, 64], H=2, h0=0.05, seed=8)
+    inp = workloads.make_prefill(spec, DEV)
+    outs = {c: gpu_prefill(inp, spec, chunk=c) for c in (16, 32, 64)}
+    again = gpu_prefill(inp, spec, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[64]["o"], again["o"]) and torch.equal(outs[64]["hT"], again["hT"])
+    for c in (16, 32):
+        assert_parity("o chunk %d vs 64" % c, to64(outs[c]["o"]), to64(outs[64]["o"]), 2e-2)
+        assert_parity("state chunk %d vs 64" % c, to64(outs[c]["hT"]), to64(outs[64]["hT"]), 2e-2)
+
+
+def test_final_state_in_place():
+    """final_state may alias initial_state."""
+    spec = spec_of([150], H=2, h0=0.05, seed=9)
+    inp = workloads.make_prefill(spec, DEV)
+    ref = gpu_prefill(inp, spec)
+    st = inp["h0"].clone()
+    o, _ = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                         cu_seqlens=inp["cu_seqlens"], scale=spec.read_scale, initial_state=st,
+                         final_state=st)
+    torch.cuda.synchronize()
+    assert torch.equal(st, ref["hT"]) and torch.equal(o, ref["o"])
+
+
+# ------------------------------------------------------------------ prologue alone
+
+@pytest.mark.parametrize("width", [1, 2, 3, 4])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_short_conv_varlen_state(width, dtype):
+    """conv with bias, history in/out, sequence resets, L2 on and off."""
+    note("short_conv width=%d %s" % (width, dtype))
+    g = torch.Generator(device=DEV).manual_seed(100 + width)
+    lengths = [1, 2, 19, 40, 0, 7]
+    cu = torch.tensor(np.cumsum([0] + lengths), dtype=torch.int32, device=DEV)
+    T, H, D, N = sum(lengths), 3, 64, len(lengths)
+    x = torch.randn(T, H * D, generator=g, device=DEV).to(dtype)
+    w = (0.5 * torch.randn(H * D, width, generator=g, device=DEV)).to(dtype)
+    b = (0.1 * torch.randn(H * D, generator=g, device=DEV)).to(dtype)
+    st = torch.randn(N, width - 1, H * D, generator=g, device=DEV).to(dtype)
+    eps = 2.0 ** -8 if dtype == torch.bfloat16 else 1e-5
+    for l2 in (False, True):
+        y, st_out = kda.short_conv(x, w, num_heads=H, head_dim=D, cu_seqlens=cu, bias=b,
+                                   conv_state=st, output_final_state=True, l2_normalize=l2)
+        torch.cuda.synchronize()
+        ry, rst = oracle.short_conv(to64(x), to64(w), cu.cpu().numpy(), to64(st), to64(b),
+                                    silu=True, return_state=True)
+        if l2:
+            ry = oracle.l2norm(ry, D, 1e-6)
+        ry = ry.reshape(T, H, D)
+        gy = to64(y)
+        bound = eps * np.abs(ry) + 1e-6
+        assert np.all(np.abs(gy - ry) <= bound), "max excess %.3e" % np.max(np.abs(gy - ry) - bound)
+        assert np.array_equal(to64(st_out), rst), "conv history out"
+    # in-place history update (state_out aliases conv_state)
+    st2 = st.clone()
+    kda.short_conv(x, w, num_heads=H, head_dim=D, cu_seqlens=cu, bias=b, conv_state=st2,
+                   state_out=st2, l2_normalize=True)
+    torch.cuda.synchronize()
+    assert torch.equal(st2, st_out)
+
+
+def test_short_conv_split_resume():
+    """Two calls carrying the conv history equal one call (bf16, width 4, L2)."""
+    g = torch.Generator(device=DEV).manual_seed(7)
+    T, H, D = 50, 2, 128
+    x = torch.randn(T, H * D, generator=g, device=DEV).bfloat16()
+    w = (0.5 * torch.randn(H * D, 4, generator=g, device=DEV)).bfloat16()
+    full, _ = kda.short_conv(x, w, num_heads=H, head_dim=D, l2_normalize=True)
+    for cut in (1, 2, 3, 17):
+        y1, st = kda.short_conv(x[:cut].contiguous(), w, num_heads=H, head_dim=D,
+                                l2_normalize=True, output_final_state=True)
+        y2, _ = kda.short_conv(x[cut:].contiguous(), w, num_heads=H, head_dim=D, l2_normalize=True,
+                               conv_state=st)
+        torch.cuda.synchronize()
+        assert torch.equal(torch.cat([y1, y2]), full), "resume at %d" % cut
+
+
+# ------------------------------------------------------------------ decode
+
+def decode_case(B, H, dk, dv, steps, dtype, seed, pairs=None):
+    spec = workloads.DecodeSpec("t", batch=B, heads=H, dk=dk, dv=dv, steps=steps, dtype=dtype,
+                                seed=seed)
+    state = workloads.make_decode_state(spec, DEV)
+    s0 = state.clone()
+    outs, ins = [], []
+    for t in range(steps):
+        inp = workloads.make_decode_step(spec, t, DEV)
+        outs.append(kda.decode_step(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], state,
+                                    scale=dk ** -0.5))
+        ins.append(inp)
+    torch.cuda.synchronize()
+    pairs = [(b, h) for b in range(B) for h in range(H)] if pairs is None else pairs
+    P = len(pairs)
+    bi = torch.tensor([p[0] for p in pairs], device=DEV)
+    hi = torch.tensor([p[1] for p in pairs], device=DEV)
+
+    def seq(key):  # [steps, B, H, ...] -> packed [P*steps, 1, ...] (pair-major)
+        x = torch.stack([i[key][bi, hi] for i in ins], dim=1)  # [P, steps, ...]
+        return to64(x.reshape(P * steps, 1, *x.shape[2:]))
+
+    cu = np.arange(P + 1) * steps
+    o, hT = oracle.recurrent(seq("q"), seq("k"), seq("v"), seq("g"),
+                             seq("beta").reshape(P * steps, 1), cu_seqlens=cu, scale=dk ** -0.5,
+                             h0=to64(s0[bi, hi]).reshape(P, 1, dk, dv))
+    got_o = torch.stack([x[bi, hi] for x in outs], dim=1).reshape(P * steps, 1, dv)
+    tol = 2e-2 if dtype == torch.bfloat16 else 1e-4
+    assert_parity("decode o", to64(got_o), o, tol)
+    assert_parity("decode state", to64(state[bi, hi]).reshape(P, 1, dk, dv), hT, tol)
+    return state
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (16, 16), (32, 128), (128, 16), (64, 64)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_decode_small(dk, dv, dtype):
+    note("decode dk=%d dv=%d %s" % (dk, dv, dtype))
+    decode_case(2, 4, dk, dv, 8, dtype, seed=dk * 3 + dv)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_decode_matches_chunk(dtype):
+    """T decode steps equal one chunk_fwd call over the same T tokens."""
+    spec = spec_of([77], H=2, dtype=dtype, h0=0.05, seed=12)
+    inp = workloads.make_prefill(spec, DEV)
+    got = gpu_prefill(inp, spec)
+    state = inp["h0"].clone()
+    os_ = []
+    for t in range(77):
+        os_.append(kda.decode_step(inp["q"][t:t + 1].contiguous(), inp["k"][t:t + 1].contiguous(),
+                                   inp["v"][t:t + 1].contiguous(), inp["g"][t:t + 1].contiguous(),
+                                   inp["beta"][t:t + 1].contiguous(), state,
+                                   scale=spec.read_scale))
+    torch.cuda.synchronize()
+    tol = 2e-2 if dtype == torch.bfloat16 else 1e-4
+    assert_parity("o decode vs chunk", to64(torch.cat(os_)), to64(got["o"]), tol)
+    assert_parity("state decode vs chunk", to64(state), to64(got["hT"]), tol)
