@@ -48,9 +48,9 @@ def library() -> ctypes.CDLL:
         lib.kda_short_conv.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp,
                                        _i32, _i32, _f32, _i32, _vp, _vp]
         lib.kda_chunk_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
-                                      _i32, _f32, _f32, _vp, _vp, _vp, _i32, _vp]
+                                      _i32, _f32, _f32, _vp, _vp, _vp, _i32, _i32, _vp]
         lib.kda_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
-                                        _vp, _i32, _vp]
+                                        _vp, _i32, _i32, _vp]
         for fn in ("kda_short_conv", "kda_chunk_fwd", "kda_decode_step"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.kda_status_string.argtypes = [ctypes.c_int]
@@ -143,11 +143,13 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               beta: torch.Tensor, *, cu_seqlens: Optional[torch.Tensor] = None,
               scale: Optional[float] = None, gate_lower_bound: float = -5.0, chunk_size: int = 64,
               initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
-              out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None
+              out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+              out_dtype: torch.dtype = torch.float32
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise KDA prefill.  q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H].
 
-    Returns o [T, H, dv] and the final states [N, H, dk, dv] (fp32) if requested.
+    Returns o [T, H, dv] (``out_dtype``, fp32 by default) and the final states
+    [N, H, dk, dv] (fp32) if requested.
     """
     _dev(q, "q")
     dt = q.dtype
@@ -166,22 +168,28 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
     if final_state is not None:
         _dev(final_state, "final_state", torch.float32, (N, H, dk, dv))
-    o = out if out is not None else torch.empty((T, H, dv), dtype=dt, device=q.device)
-    _dev(o, "out", dt, (T, H, dv))
+    if out is not None:
+        out_dtype = out.dtype
+    if out_dtype not in _DTYPES:
+        raise ValueError("out_dtype must be bf16 or fp32")
+    o = out if out is not None else torch.empty((T, H, dv), dtype=out_dtype, device=q.device)
+    _dev(o, "out", out_dtype, (T, H, dv))
     sc = dk ** -0.5 if scale is None else float(scale)
     _check(library().kda_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,
         int(chunk_size), sc, float(gate_lower_bound), _ptr(initial_state), _ptr(final_state),
-        _ptr(o), _DTYPES[dt], _stream(q)))
+        _ptr(o), _DTYPES[dt], _DTYPES[out_dtype], _stream(q)))
     return o, final_state
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                 beta: torch.Tensor, state: torch.Tensor, *, scale: Optional[float] = None,
-                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None,
+                out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
     """One recurrent step; ``state`` [B, H, dk, dv] fp32 is updated in place.
 
-    q, k, g: [B, H, dk]; v: [B, H, dv]; beta: [B, H].  Returns o [B, H, dv].
+    q, k, g: [B, H, dk]; v: [B, H, dv]; beta: [B, H].  Returns o [B, H, dv]
+    (``out_dtype``, fp32 by default).
     """
     _dev(q, "q")
     dt = q.dtype
@@ -194,10 +202,14 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     _dev(g, "g", torch.float32, (B, H, dk))
     _dev(beta, "beta", torch.float32, (B, H))
     _dev(state, "state", torch.float32, (B, H, dk, dv))
-    o = out if out is not None else torch.empty((B, H, dv), dtype=dt, device=q.device)
-    _dev(o, "out", dt, (B, H, dv))
+    if out is not None:
+        out_dtype = out.dtype
+    if out_dtype not in _DTYPES:
+        raise ValueError("out_dtype must be bf16 or fp32")
+    o = out if out is not None else torch.empty((B, H, dv), dtype=out_dtype, device=q.device)
+    _dev(o, "out", out_dtype, (B, H, dv))
     sc = dk ** -0.5 if scale is None else float(scale)
     _check(library().kda_decode_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), B, H, dk, dv, sc, _ptr(o),
-        _DTYPES[dt], _stream(q)))
+        _DTYPES[dt], _DTYPES[out_dtype], _stream(q)))
     return o

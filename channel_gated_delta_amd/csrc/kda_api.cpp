@@ -86,7 +86,7 @@ KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, 
                                    int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
                                    int32_t chunk_size, float scale, float gate_lower_bound,
                                    const float *initial_state, float *final_state, void *o,
-                                   kda_dtype_t dtype, void *stream) {
+                                   kda_dtype_t dtype, kda_dtype_t out_dtype, void *stream) {
     g_last_error[0] = '\0';
     if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o))
         return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: NULL q/k/v/g/beta/o");
@@ -94,7 +94,10 @@ KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, 
         return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: bad sizes");
     if (!cu_seqlens && num_seqs != 1)
         return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: cu_seqlens NULL needs num_seqs == 1");
-    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: bad dtype");
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype))
+        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: bad dtype");
+    if (dtype == KDA_DTYPE_F32 && out_dtype != KDA_DTYPE_F32)
+        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: fp32 inputs need an fp32 output");
     if (!isfinite(scale)) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: scale not finite");
     if (o && (o == q || o == k || o == v || o == (const void *)g || o == (const void *)beta))
         return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: o aliases an input");
@@ -109,24 +112,28 @@ KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, 
         return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: grid too large");
     kda::ChunkArgs a{q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, dk, dv,
                      chunk_size, scale, gate_lower_bound, initial_state, final_state, o};
-    const bool bf = dtype == KDA_DTYPE_BF16;
+    auto launcher = dtype == KDA_DTYPE_F32            ? kda::launch_chunk_f32
+                    : out_dtype == KDA_DTYPE_F32      ? kda::launch_chunk_bf16_f32out
+                                                      : kda::launch_chunk_bf16_bf16out;
     bool ok = false;
-    (void)(bf ? kda::launch_chunk_bf16 : kda::launch_chunk_f32)(a, (hipStream_t)stream, false, &ok);
+    (void)launcher(a, (hipStream_t)stream, false, &ok);
     if (!ok) return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: no kernel for dk=%d dv=%d", dk, dv);
-    return from_hip((bf ? kda::launch_chunk_bf16 : kda::launch_chunk_f32)(a, (hipStream_t)stream,
-                                                                           true, &ok),
-                    "kda_chunk_fwd");
+    return from_hip(launcher(a, (hipStream_t)stream, true, &ok), "kda_chunk_fwd");
 }
 
 KDA_API kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const float *g,
                                      const float *beta, float *state, int32_t batch,
                                      int32_t num_heads, int32_t dk, int32_t dv, float scale,
-                                     void *o, kda_dtype_t dtype, void *stream) {
+                                     void *o, kda_dtype_t dtype, kda_dtype_t out_dtype,
+                                     void *stream) {
     g_last_error[0] = '\0';
     if (batch > 0 && (!q || !k || !v || !g || !beta || !state || !o))
         return fail(KDA_ERR_INVALID_ARG, "kda_decode_step: NULL pointer");
     if (batch < 0 || num_heads < 1) return fail(KDA_ERR_INVALID_ARG, "kda_decode_step: bad sizes");
-    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "kda_decode_step: bad dtype");
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype))
+        return fail(KDA_ERR_INVALID_ARG, "kda_decode_step: bad dtype");
+    if (dtype == KDA_DTYPE_F32 && out_dtype != KDA_DTYPE_F32)
+        return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: fp32 inputs need an fp32 output");
     if (!isfinite(scale)) return fail(KDA_ERR_INVALID_ARG, "kda_decode_step: scale not finite");
     if (o && (o == q || o == k || o == v || o == (const void *)g || o == (const void *)beta ||
               o == (const void *)state))
@@ -135,7 +142,8 @@ KDA_API kda_status_t kda_decode_step(const void *q, const void *k, const void *v
         return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: dk/dv not in {16,32,64,128}");
     if ((int64_t)batch * num_heads > ((int64_t)1 << 31) - 1)
         return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: grid too large");
-    kda::DecodeArgs a{q, k, v, g, beta, state, batch, num_heads, dk, dv, scale, o};
+    kda::DecodeArgs a{q, k, v, g, beta, state, batch, num_heads, dk, dv, scale, o,
+                      out_dtype == KDA_DTYPE_F32};
     return from_hip(kda::launch_decode_step(a, dtype == KDA_DTYPE_BF16, (hipStream_t)stream),
                     "kda_decode_step");
 }

@@ -1,5 +1,5 @@
 // kda_chunk.cuh -- chunkwise-parallel KDA prefill kernel (included by the
-// per-dtype translation units kda_chunk_bf16.hip / kda_chunk_f32.hip).
+// per-dtype translation units kda_chunk_*.hip).
 //
 // Semantics: the token recurrence of [Walkthrough] 第三站-第五站 (decay the rows
 // of S by exp(g_t), predict S^T k_t, write beta_t k_t (v_t - S^T k_t)^T, read
@@ -8,10 +8,10 @@
 // transitions compose into one chunk-level transform).
 //
 // Chunk algebra (derived from the recurrence; state S0 entering a chunk of n
-// tokens, G_t = sum_{j<=t} g_j per key channel, all exponentials of differences):
+// tokens, G_t = sum_{j<=t} g_j per key channel, exponentials of differences only):
 //   A_ti = sum_c k_tc k_ic e^{G_tc - G_ic}  (i < t),   P_ti = sum_c q_tc k_ic e^{G_tc - G_ic}  (i <= t)
-//   T    = (I + diag(beta) A)^{-1},  Tb = T diag(beta)
-//   W    = Tb (K * e^{G}),  U~ = Tb V,  U = U~ - W S0
+//   Tb   = (I + diag(beta) A)^{-1} diag(beta)
+//   U    = Tb (V - (K * e^{G}) S0)
 //   O    = scale (Q * e^{G}) S0 + scale P U
 //   S    = diag(e^{G_n}) S0 + (K * e^{G_n - G})^T U
 //
@@ -19,21 +19,31 @@
 // slice of BV columns) and walks the chunks of its sequence; value columns of S
 // evolve independently, so slicing multiplies the parallelism of a head.  The
 // fp32 state slice lives in MFMA accumulator registers for the whole sequence
-// and is mirrored into LDS in the operand dtype once per chunk.  All products
-// run on 16x16 MFMA tiles (bf16 in, fp32 accumulate; fp32 MFMA for the fp32
-// dtype); the 64x64 unit-lower-triangular inverse is done in fp32 (16x16
-// forward substitution per diagonal block, then blockwise fp32 MFMA merges).
+// and is mirrored into LDS in the operand dtype once per chunk.  Products run
+// on 16x16 MFMA tiles (bf16 in / fp32 accumulate; fp32 MFMA for fp32 inputs);
+// the unit-lower-triangular inverse is done in fp32 (16x16 forward substitution
+// per diagonal block, then blockwise fp32 MFMA merges).
+//
+// Precision of the bf16 path.  The outputs are heavy-tailed (the largest |o| is
+// ~10x the rms), so a single bf16 rounding of a product that feeds o or S
+// directly already costs ~2^-9 * 10 of the rms.  Those products therefore use
+// split operands x = hi + lo (both bf16, |lo| <= 2^-9 |x|) and the three-term
+// product hi*hi + hi*lo + lo*hi (~2^-16 relative): Tb (V - Kd S), P U and
+// Kr^T U.  The Gram matrices stay single bf16 products except the diagonal of
+// P (the current token's own term scale q_t . k_t, no decay), which is
+// recomputed exactly in fp32.  S, Qd and Kd are single bf16 operands.
 //
 // Decay numerics ([Walkthrough] 彩蛋: products of retention factors and their
-// reciprocals must stay inside the floating-point range).  The intra-chunk Gram
-// matrices factor e^{G_t - G_i} through 16-token sub-tiles referenced at the
-// tile's middle row m: rows use e^{G_t - G_m}, columns e^{G_m - G_i}, which are
-// bounded by e^{8|lb|} (finite for lb >= -10); off-diagonal tile pairs (R, I)
-// multiply the column operand by the per-channel boundary factor
-// e^{G_{m_R} - G_{m_I}} <= 1.  Every other factor (e^{G_t}, e^{G_n - G_t},
-// e^{G_n}) is <= 1 and is exponentiated directly.  Exponents are kept in log2
-// units and evaluated with v_exp_f32.
+// reciprocals must stay inside the floating-point range).  The Gram matrices
+// factor e^{G_t - G_i} through 16-token sub-tiles referenced at the tile's
+// middle row m: rows use e^{G_t - G_m}, columns e^{G_m - G_i}, both bounded by
+// e^{8|lb|} (finite for lb >= -10); off-diagonal tile pairs (R, I) scale the
+// column operand by the per-channel boundary factor e^{G_{m_R} - G_{m_I}} <= 1.
+// Every other factor (e^{G_t}, e^{G_n - G_t}, e^{G_n}) is <= 1 and is
+// exponentiated directly.  Exponents are in log2 units (v_exp_f32).
 #pragma once
+
+#include <type_traits>
 
 #include "kda_device.cuh"
 
@@ -42,43 +52,49 @@ namespace kda {
 template <class T, int DK_, int BV_, int C_>
 struct ChunkCfg {
     static constexpr int DK = DK_, BV = BV_, C = C_;
+    static constexpr bool kSplit = std::is_same<T, bf16>::value;
+    static constexpr int NSPLIT = kSplit ? 2 : 1;
     static constexpr int NW = 4, NT = NW * kWave;
     static constexpr int NTC = C / 16, NTK = DK / 16, NTV = BV / 16;
     static constexpr int VEC = 16 / (int)sizeof(T);             // elements per 16-byte vector
     static constexpr int PAD = 16 / (int)sizeof(T);             // LDS row padding (elements)
     static constexpr int LDK = DK + PAD;                        // [*][DK] operand rows
     static constexpr int LDC = C + PAD;                         // [*][C] operand rows
-    static constexpr int LDA = C + 1;                           // fp32 A / T matrix rows
+    static constexpr int LDA = C + 4;                           // fp32 [C][C] rows
     static constexpr int KPL_DK = KplFor<T, DK>::value;
     static constexpr int KPL_C = KplFor<T, C>::value;
     static constexpr int NPAIR = NTC * (NTC - 1) / 2;
+    static constexpr int NP = NT / DK;                          // token parts per channel
+    static constexpr int RP = C / NP;                           // tokens per part
     static constexpr int NS_TILES = NTK * NTV, NSW = (NS_TILES + NW - 1) / NW;
     static constexpr int NU_TILES = NTC * NTV, NUW = (NU_TILES + NW - 1) / NW;
+    static_assert(NP * DK == NT && NP * RP == C, "channel/token split");
 
     static constexpr size_t al(size_t x) { return (x + 15) & ~(size_t)15; }
     static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
-    static constexpr size_t szQ = al((size_t)C * LDK * sizeof(T));
-    static constexpr size_t szK = al(mx((size_t)C * LDK, (size_t)DK * LDC) * sizeof(T));
-    static constexpr size_t szX = al((size_t)C * LDK * sizeof(T));
-    static constexpr size_t szKdT = al((size_t)DK * LDC * sizeof(T));
-    static constexpr size_t szTb = al((size_t)C * LDC * sizeof(T));
-    static constexpr size_t szG = al(mx((size_t)C * DK * 4, szKdT + szTb));
-    static constexpr size_t szV = al((size_t)BV * LDC * sizeof(T));
-    static constexpr size_t szA = al((size_t)C * LDA * 4);
-    static constexpr size_t szP = al((size_t)C * LDC * sizeof(T));
-    static constexpr size_t szU = al((size_t)BV * LDC * sizeof(T));
-    static constexpr size_t szS = al((size_t)BV * LDK * sizeof(T));
+    static constexpr size_t szCK = al((size_t)C * LDK * sizeof(T));      // [C][DK]
+    static constexpr size_t szKC = al((size_t)DK * LDC * sizeof(T));     // [DK][C]
+    static constexpr size_t szVC = al((size_t)BV * LDC * sizeof(T));     // [BV][C]
+    static constexpr size_t szCC = al((size_t)C * LDA * 4);              // fp32 [C][C]
+    static constexpr size_t szS = al((size_t)BV * LDK * sizeof(T));      // [BV][DK]
     static constexpr size_t szY = al((size_t)(NTC > 1 ? NTC - 1 : 1) * 256 * 4);
     static constexpr size_t szSmall =
-        al((size_t)(C + (NPAIR > 0 ? NPAIR : 1) * DK + DK) * 4);
-    static constexpr size_t oQ = 0, oK = oQ + szQ, oX = oK + szK, oG = oX + szX, oV = oG + szG,
-                            oA = oV + szV, oP = oA + szA, oU = oP + szP, oS = oU + szU,
-                            oY = oS + szS, oSmall = oY + szY;
+        al((size_t)(2 * C + (NPAIR > 0 ? NPAIR : 1) * DK + (NTC + 2 + NP) * DK) * 4);
+    static constexpr size_t oQ = 0;                    // raw q -> q*Dr -> scale q e^G
+    static constexpr size_t oK = oQ + szCK;            // raw k -> k*Dr -> k e^G
+    static constexpr size_t oX = oK + szCK;            // k*Dc, then (k e^{Gn-G})^T hi/lo
+    static constexpr size_t oV = oX + mx(szCK, NSPLIT * szKC);
+    static constexpr size_t oA = oV + szVC;            // A -> T diag(beta)   (fp32)
+    static constexpr size_t oP = oA + szCC;            // scale * P           (fp32)
+    static constexpr size_t oE = oP + szCC;            // (V - Kd S)^T hi/lo, then U^T hi/lo
+    static constexpr size_t oS = oE + NSPLIT * szVC;   // S^T operand copy
+    static constexpr size_t oY = oS + szS;
+    static constexpr size_t oSmall = oY + szY;
     static constexpr size_t kLds = oSmall + szSmall;
     static constexpr bool kFits = kLds <= 160 * 1024;
 };
 
-// Per-channel block offset for a packed batch; cu == NULL is one sequence.
+// Packed-sequence offset i clamped to [0, total]; cu == NULL is one sequence.
 __device__ __forceinline__ int64_t chunk_seq_off(const int32_t *cu, int i, int64_t total) {
     if (!cu) return i == 0 ? 0 : total;
     return min((int64_t)max(cu[i], 0), total);
@@ -94,36 +110,101 @@ __device__ __forceinline__ void scale_frag(bf16x8 &f, const float *s) {
     for (int e = 0; e < 8; ++e) f[e] = (bf16)((float)f[e] * s[e]);
 }
 
-template <class T, int DK, int BV, int C>
+// A-operand fragment read from an fp32 LDS matrix [rows][ld] and split into
+// bf16 hi + lo parts (KPL consecutive k per lane, as load_frag).
+template <int KPL>
+__device__ __forceinline__ void load_frag_split(const float *M, int ld, int row0, int k0, int lane,
+                                                typename Frag<bf16, KPL>::type &hi,
+                                                typename Frag<bf16, KPL>::type &lo) {
+    const float *p = M + (row0 + (lane & 15)) * ld + k0 + (lane >> 4) * KPL;
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) {
+        const float x = p[e];
+        const bf16 h = (bf16)x;
+        hi[e] = h;
+        lo[e] = (bf16)(x - (float)h);
+    }
+}
+
+// D += A B^T-style tile product where A comes from an fp32 LDS matrix and B from
+// k-contiguous hi (and lo) operand matrices in T.  With T = bf16 the product is
+// the three-term split product; with T = fp32 it is a plain fp32 product.
+template <class T, int KPL>
+__device__ __forceinline__ f32x4 tile_mma_f32a(f32x4 acc, const float *A, int lda, int arow0,
+                                               const T *Bh, const T *Bl, int ldb, int brow0,
+                                               int kend, int lane) {
+    for (int k0 = 0; k0 < kend; k0 += 4 * KPL) {
+        if constexpr (std::is_same<T, bf16>::value) {
+            typename Frag<bf16, KPL>::type ah, al;
+            load_frag_split<KPL>(A, lda, arow0, k0, lane, ah, al);
+            auto bh = load_frag<T, KPL>(Bh, ldb, brow0, k0, lane);
+            auto bl = load_frag<T, KPL>(Bl, ldb, brow0, k0, lane);
+            acc = mma(ah, bh, acc);
+            acc = mma(ah, bl, acc);
+            acc = mma(al, bh, acc);
+        } else {
+            const float a = A[(arow0 + (lane & 15)) * lda + k0 + (lane >> 4)];
+            auto b = load_frag<T, KPL>(Bh, ldb, brow0, k0, lane);
+            acc = mma(a, b, acc);
+        }
+    }
+    return acc;
+}
+
+// Same with both operands as (hi, lo) pairs in T (three-term product for bf16).
+template <class T, int KPL>
+__device__ __forceinline__ f32x4 tile_mma_split(f32x4 acc, const T *Ah, const T *Al, int lda,
+                                                int arow0, const T *Bh, const T *Bl, int ldb,
+                                                int brow0, int kend, int lane) {
+    for (int k0 = 0; k0 < kend; k0 += 4 * KPL) {
+        auto ah = load_frag<T, KPL>(Ah, lda, arow0, k0, lane);
+        auto bh = load_frag<T, KPL>(Bh, ldb, brow0, k0, lane);
+        acc = mma(ah, bh, acc);
+        if constexpr (std::is_same<T, bf16>::value) {
+            auto al = load_frag<T, KPL>(Al, lda, arow0, k0, lane);
+            auto bl = load_frag<T, KPL>(Bl, ldb, brow0, k0, lane);
+            acc = mma(ah, bl, acc);
+            acc = mma(al, bh, acc);
+        }
+    }
+    return acc;
+}
+
+template <class T, class TO, int DK, int BV, int C>
 __global__ __launch_bounds__(256, 1)
 void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                   const float *__restrict__ g, const float *__restrict__ beta,
                   const int32_t *__restrict__ cu_seqlens, int64_t total, int H, int DV,
                   float scale, const float *__restrict__ h0, float *__restrict__ hT,
-                  T *__restrict__ o, int units, int nslice) {
+                  TO *__restrict__ o, int units, int nslice) {
     using Cfg = ChunkCfg<T, DK, BV, C>;
+    constexpr bool SPLIT = Cfg::kSplit;
     constexpr int NW = Cfg::NW, NT = Cfg::NT, NTC = Cfg::NTC, NTK = Cfg::NTK, NTV = Cfg::NTV;
     constexpr int VEC = Cfg::VEC, LDK = Cfg::LDK, LDC = Cfg::LDC, LDA = Cfg::LDA;
-    constexpr int KPL_DK = Cfg::KPL_DK, KPL_C = Cfg::KPL_C;
-    constexpr int KSTEP_C = 4 * KPL_C;
-    typedef typename Vec16<T>::type VT;       // 16-byte vector of T
+    constexpr int KPL_DK = Cfg::KPL_DK, KPL_C = Cfg::KPL_C, KSTEP_C = 4 * KPL_C;
+    constexpr int RP = Cfg::RP;
+    typedef typename Vec16<T>::type VT;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::kLds];
-    T *sQ = reinterpret_cast<T *>(smem + Cfg::oQ);     // raw q -> q*Dr -> scale*q*e^G
-    T *sK = reinterpret_cast<T *>(smem + Cfg::oK);     // raw k -> k*Dr -> (k*e^{Gn-G})^T
-    T *sX = reinterpret_cast<T *>(smem + Cfg::oX);     // k*Dc -> -W   (Dr, Dc: sub-tile factors)
-    float *sGam = reinterpret_cast<float *>(smem + Cfg::oG);  // G (log2 units)
-    T *sKdT = reinterpret_cast<T *>(smem + Cfg::oG);          // (k*e^G)^T   (reuses G)
-    T *sTb = reinterpret_cast<T *>(smem + Cfg::oG + Cfg::szKdT);  // T diag(beta)
-    T *sVT = reinterpret_cast<T *>(smem + Cfg::oV);    // V^T slice
-    float *sA = reinterpret_cast<float *>(smem + Cfg::oA);  // A -> T (fp32)
-    T *sP = reinterpret_cast<T *>(smem + Cfg::oP);     // scale * masked P
-    T *sUT = reinterpret_cast<T *>(smem + Cfg::oU);    // U^T
-    T *sST = reinterpret_cast<T *>(smem + Cfg::oS);    // S^T (operand copy of the state)
-    float *sY = reinterpret_cast<float *>(smem + Cfg::oY);  // inverse scratch
+    T *sQ = reinterpret_cast<T *>(smem + Cfg::oQ);
+    T *sK = reinterpret_cast<T *>(smem + Cfg::oK);
+    T *sX = reinterpret_cast<T *>(smem + Cfg::oX);                    // k*Dc (Gram columns)
+    T *sKrH = reinterpret_cast<T *>(smem + Cfg::oX);                  // (k e^{Gn-G})^T hi
+    T *sKrL = reinterpret_cast<T *>(smem + Cfg::oX + (SPLIT ? Cfg::szKC : 0));
+    T *sVT = reinterpret_cast<T *>(smem + Cfg::oV);                   // V^T slice
+    float *sA = reinterpret_cast<float *>(smem + Cfg::oA);            // A -> Tb
+    float *sPf = reinterpret_cast<float *>(smem + Cfg::oP);           // scale * P
+    T *sEH = reinterpret_cast<T *>(smem + Cfg::oE);                   // E^T / U^T hi
+    T *sEL = reinterpret_cast<T *>(smem + Cfg::oE + (SPLIT ? Cfg::szVC : 0));
+    T *sST = reinterpret_cast<T *>(smem + Cfg::oS);                   // S^T operand
+    float *sY = reinterpret_cast<float *>(smem + Cfg::oY);
     float *sBeta = reinterpret_cast<float *>(smem + Cfg::oSmall);
-    float *sBnd = sBeta + C;                            // e^{G_mR - G_mI}, I < R
-    float *sEGn = sBnd + (Cfg::NPAIR > 0 ? Cfg::NPAIR : 1) * DK;  // e^{G_last}
+    float *sPd = sBeta + C;                                            // scale q_t . k_t
+    float *sBnd = sPd + C;                                             // e^{G_mR - G_mI}
+    float *sGm = sBnd + (Cfg::NPAIR > 0 ? Cfg::NPAIR : 1) * DK;        // G at tile middles
+    float *sGl = sGm + NTC * DK;                                       // G at the last row
+    float *sEGn = sGl + DK;                                            // e^{G_last}
+    float *sTot = sEGn + DK;                                           // part sums of g
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
 
@@ -169,20 +250,32 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
     };
     store_state_operand();
 
+    // channel-owner mapping used for the decay factors: channel c, tokens [part*RP, +RP)
+    const int cc = tid % DK, part = tid / DK;
+
     for (int64_t c0 = bos; c0 < eos; c0 += C) {
         const int nt = (int)min((int64_t)C, eos - c0);
 
         // ================= L: load the chunk (rows >= nt are zero) =================
-        for (int idx = tid; idx < C * (DK / VEC); idx += NT) {
-            const int r = idx / (DK / VEC), cv = idx % (DK / VEC);
-            VT qv = VT{}, kv = VT{};
-            if (r < nt) {
-                const size_t off = (size_t)(c0 + r) * rowQK + (size_t)h * DK + cv * VEC;
-                qv = *reinterpret_cast<const VT *>(q + off);
-                kv = *reinterpret_cast<const VT *>(k + off);
+        {
+            constexpr int LPR = DK / VEC;   // lanes per row (power of two <= 32)
+            for (int idx = tid; idx < C * LPR; idx += NT) {
+                const int r = idx / LPR, cv = idx % LPR;
+                VT qv = VT{}, kv = VT{};
+                if (r < nt) {
+                    const size_t off = (size_t)(c0 + r) * rowQK + (size_t)h * DK + cv * VEC;
+                    qv = *reinterpret_cast<const VT *>(q + off);
+                    kv = *reinterpret_cast<const VT *>(k + off);
+                }
+                *reinterpret_cast<VT *>(sQ + r * LDK + cv * VEC) = qv;
+                *reinterpret_cast<VT *>(sK + r * LDK + cv * VEC) = kv;
+                // exact diagonal of P: scale * q_r . k_r (products of bf16 are exact in fp32)
+                float dot = 0.f;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) dot += to_f32(qv[e]) * to_f32(kv[e]);
+                dot = group_sum<LPR>(dot);
+                if (cv == 0) sPd[r] = scale * dot;
             }
-            *reinterpret_cast<VT *>(sQ + r * LDK + cv * VEC) = qv;
-            *reinterpret_cast<VT *>(sK + r * LDK + cv * VEC) = kv;
         }
         for (int idx = tid; idx < C * (BV / VEC); idx += NT) {
             const int r = idx / (BV / VEC), cv = idx % (BV / VEC);
@@ -194,82 +287,75 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
             for (int e = 0; e < VEC; ++e) sVT[(cv * VEC + e) * LDC + r] = vv[e];
         }
         if (tid < C) sBeta[tid] = tid < nt ? beta[(size_t)(c0 + tid) * H + h] : 0.f;
+
+        // cumulative log2-decay of channel cc over this thread's tokens (registers)
+        float gam[RP];
         {
-            // cumulative log2-decay per key channel: NP parts of RP rows, then a prefix fix-up
-            constexpr int NP = NT / DK, RP = C / NP;
-            static_assert(NP * DK == NT && NP * RP == C, "cumsum split");
-            const int c = tid % DK, part = tid / DK;
             float gv[RP];
 #pragma unroll
             for (int j = 0; j < RP; ++j) {
                 const int r = part * RP + j;
-                gv[j] = r < nt ? g[(size_t)(c0 + r) * rowQK + (size_t)h * DK + c] : 0.f;
+                gv[j] = r < nt ? g[(size_t)(c0 + r) * rowQK + (size_t)h * DK + cc] : 0.f;
             }
             float acc = 0.f;
 #pragma unroll
             for (int j = 0; j < RP; ++j) {
                 acc += gv[j] * kLog2e;
-                sGam[(part * RP + j) * DK + c] = acc;
+                gam[j] = acc;
             }
-            if constexpr (NP > 1) {
-                __syncthreads();
-                float off = 0.f;
-                for (int p = 0; p < part; ++p) off += sGam[((p + 1) * RP - 1) * DK + c];
-                __syncthreads();
+            sTot[part * DK + cc] = acc;
+        }
+        __syncthreads();
+        {
+            float off = 0.f;
+            for (int p = 0; p < part; ++p) off += sTot[p * DK + cc];
 #pragma unroll
-                for (int j = 0; j < RP; ++j) sGam[(part * RP + j) * DK + c] += off;
+            for (int j = 0; j < RP; ++j) {
+                gam[j] += off;
+                const int r = part * RP + j;
+                if ((r & 15) == 8) sGm[(r >> 4) * DK + cc] = gam[j];
+                if (r == C - 1) sGl[cc] = gam[j];
             }
         }
         __syncthreads();
 
         // ================= F: decay factors =================
         // Gram operands to LDS: q e^{G_t-G_m}, k e^{G_t-G_m}, k e^{G_m-G_t} (m = middle
-        // row of t's 16-token tile).  Chunk-level operands kept in registers until
-        // the Gram products are done: scale q e^{G_t}, k e^{G_t}, k e^{G_n-G_t}.
-        constexpr int PER = (C * (DK / VEC) + NT - 1) / NT;
-        VT rQd[PER], rKd[PER], rKr[PER];
+        // row of t's 16-token tile).  Chunk-level operands stay in registers until the
+        // Gram products are done: scale q e^{G_t}, k e^{G_t}, k e^{G_n-G_t} (hi, lo).
+        T rQd[RP], rKd[RP], rKrH[RP], rKrL[RP];
+        {
+            const float gl = sGl[cc];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int idx = tid + j * NT;
-            if (idx < C * (DK / VEC)) {
-                const int r = idx / (DK / VEC), cv = idx % (DK / VEC);
-                const int m = (r / 16) * 16 + 8;
-                const VT qv = *reinterpret_cast<const VT *>(sQ + r * LDK + cv * VEC);
-                const VT kv = *reinterpret_cast<const VT *>(sK + r * LDK + cv * VEC);
-                VT qd, kd, kc;
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    const int c = cv * VEC + e;
-                    const float gt = sGam[r * DK + c];
-                    const float d = gt - sGam[m * DK + c];
-                    const float dr = exp2_clamped(d), dc = exp2_clamped(-d);
-                    const float eg = exp2_clamped(gt);
-                    const float egr = exp2_clamped(sGam[(C - 1) * DK + c] - gt);
-                    const float qf = to_f32(qv[e]), kf = to_f32(kv[e]);
-                    qd[e] = from_f32<T>(qf * dr);
-                    kd[e] = from_f32<T>(kf * dr);
-                    kc[e] = from_f32<T>(kf * dc);
-                    rQd[j][e] = from_f32<T>(qf * eg * scale);
-                    rKd[j][e] = from_f32<T>(kf * eg);
-                    rKr[j][e] = from_f32<T>(kf * egr);
-                }
-                *reinterpret_cast<VT *>(sQ + r * LDK + cv * VEC) = qd;
-                *reinterpret_cast<VT *>(sK + r * LDK + cv * VEC) = kd;
-                *reinterpret_cast<VT *>(sX + r * LDK + cv * VEC) = kc;
+            for (int j = 0; j < RP; ++j) {
+                const int r = part * RP + j;
+                const float gt = gam[j];
+                const float d = gt - sGm[(r >> 4) * DK + cc];
+                const float dr = exp2_clamped(d), dc = exp2_clamped(-d);
+                const float eg = exp2_clamped(gt), egr = exp2_clamped(gl - gt);
+                const float qf = to_f32(sQ[r * LDK + cc]), kf = to_f32(sK[r * LDK + cc]);
+                sQ[r * LDK + cc] = from_f32<T>(qf * dr);
+                sK[r * LDK + cc] = from_f32<T>(kf * dr);
+                sX[r * LDK + cc] = from_f32<T>(kf * dc);
+                rQd[j] = from_f32<T>(qf * eg * scale);
+                rKd[j] = from_f32<T>(kf * eg);
+                const float kr = kf * egr;
+                rKrH[j] = from_f32<T>(kr);
+                rKrL[j] = from_f32<T>(kr - to_f32(rKrH[j]));
             }
-        }
-        for (int c = tid; c < DK; c += NT) {
-            sEGn[c] = exp2_clamped(sGam[(C - 1) * DK + c]);
+            if (part == 0) {
+                sEGn[cc] = exp2_clamped(gl);
 #pragma unroll
-            for (int R = 1; R < NTC; ++R)
+                for (int R = 1; R < NTC; ++R)
 #pragma unroll
-                for (int I = 0; I < R; ++I)
-                    sBnd[(R * (R - 1) / 2 + I) * DK + c] =
-                        exp2_clamped(sGam[(R * 16 + 8) * DK + c] - sGam[(I * 16 + 8) * DK + c]);
+                    for (int I = 0; I < R; ++I)
+                        sBnd[(R * (R - 1) / 2 + I) * DK + cc] =
+                            exp2_clamped(sGm[R * DK + cc] - sGm[I * DK + cc]);
+            }
         }
         __syncthreads();
 
-        // ================= G: Gram tiles A (strict lower) and P (lower) =================
+        // ================= G: Gram tiles A (strict lower) and P (lower, exact diagonal) ==
         for (int p = wave; p < NTC * NTC; p += NW) {
             const int R = p / NTC, I = p % NTC;
             f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
@@ -288,25 +374,19 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
             for (int r = 0; r < 4; ++r) {
                 const int row = R * 16 + acc_row(lane, r), col = I * 16 + acc_col(lane);
                 sA[row * LDA + col] = row > col ? accA[r] : 0.f;
-                sP[row * LDC + col] = from_f32<T>(row >= col ? scale * accP[r] : 0.f);
+                sPf[row * LDA + col] = row > col ? scale * accP[r] : (row == col ? sPd[row] : 0.f);
             }
         }
         __syncthreads();
 
         // ================= X: chunk-level operands; inverse diagonal blocks =================
-        // The Gram operands and G are dead: Qd over q*Dr, (k e^G)^T over G, (k e^{Gn-G})^T over k*Dr.
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int idx = tid + j * NT;
-            if (idx < C * (DK / VEC)) {
-                const int r = idx / (DK / VEC), cv = idx % (DK / VEC);
-                *reinterpret_cast<VT *>(sQ + r * LDK + cv * VEC) = rQd[j];
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    sKdT[(cv * VEC + e) * LDC + r] = rKd[j][e];
-                    sK[(cv * VEC + e) * LDC + r] = rKr[j][e];
-                }
-            }
+        for (int j = 0; j < RP; ++j) {
+            const int r = part * RP + j;
+            sQ[r * LDK + cc] = rQd[j];
+            sK[r * LDK + cc] = rKd[j];
+            sKrH[cc * LDC + r] = rKrH[j];
+            if constexpr (SPLIT) sKrL[cc * LDC + r] = rKrL[j];
         }
         // diagonal 16x16 blocks of (I + diag(beta) A)^{-1}: lane i builds column i
         for (int R = wave; R < NTC; R += NW) {
@@ -356,71 +436,80 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
             }
             __syncthreads();
         }
-
-        // Tb = T diag(beta) in the operand dtype
+        // Tb = T diag(beta), in place (fp32)
         for (int idx = tid; idx < C * C; idx += NT) {
             const int r = idx / C, i = idx % C;
-            sTb[r * LDC + i] = from_f32<T>(sA[r * LDA + i] * sBeta[i]);
+            sA[r * LDA + i] *= sBeta[i];
         }
-        __syncthreads();
 
-        // ================= W = -Tb (K e^G) -> sX ;  U~ = Tb V -> registers =================
-        for (int id = wave; id < NTC * NTK; id += NW) {
-            const int R = id / NTK, ck = id % NTK;
-            const int kend = ((R + 1) * 16 + KSTEP_C - 1) / KSTEP_C * KSTEP_C;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = tile_mma<T, KPL_C>(acc, sTb, LDC, R * 16, sKdT, LDC, ck * 16, 0,
-                                     kend < C ? kend : C, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sX[(R * 16 + acc_row(lane, r)) * LDK + ck * 16 + acc_col(lane)] = from_f32<T>(-acc[r]);
-        }
+        // ================= E = V - Kd S -> E^T (hi, lo);  O = Qd S =================
         f32x4 Uacc[Cfg::NUW], Oacc[Cfg::NUW];
 #pragma unroll
         for (int i = 0; i < Cfg::NUW; ++i) {
             const int id = wave + i * NW;
             Uacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (id < Cfg::NU_TILES) {
-                const int R = id / NTV, cv = id % NTV;
-                const int kend = ((R + 1) * 16 + KSTEP_C - 1) / KSTEP_C * KSTEP_C;
-                Uacc[i] = tile_mma<T, KPL_C>(Uacc[i], sTb, LDC, R * 16, sVT, LDC, cv * 16, 0,
-                                             kend < C ? kend : C, lane);
-            }
-        }
-        __syncthreads();
-
-        // ================= U = U~ - W S ;  O = Qd S =================
-#pragma unroll
-        for (int i = 0; i < Cfg::NUW; ++i) {
-            const int id = wave + i * NW;
             Oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (id < Cfg::NU_TILES) {
                 const int R = id / NTV, cv = id % NTV;
-                Uacc[i] = tile_mma<T, KPL_DK>(Uacc[i], sX, LDK, R * 16, sST, LDK, cv * 16, 0, DK, lane);
-                Oacc[i] = tile_mma<T, KPL_DK>(Oacc[i], sQ, LDK, R * 16, sST, LDK, cv * 16, 0, DK, lane);
+                f32x4 ks = tile_mma<T, KPL_DK>(f32x4{0.f, 0.f, 0.f, 0.f}, sK, LDK, R * 16, sST,
+                                               LDK, cv * 16, 0, DK, lane);
+                Oacc[i] = tile_mma<T, KPL_DK>(Oacc[i], sQ, LDK, R * 16, sST, LDK, cv * 16, 0, DK,
+                                              lane);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sUT[(cv * 16 + acc_col(lane)) * LDC + R * 16 + acc_row(lane, r)] =
-                        from_f32<T>(Uacc[i][r]);
+                for (int r = 0; r < 4; ++r) {
+                    const int t = R * 16 + acc_row(lane, r), vc = cv * 16 + acc_col(lane);
+                    const float e = to_f32(sVT[vc * LDC + t]) - ks[r];
+                    const T eh = from_f32<T>(e);
+                    sEH[vc * LDC + t] = eh;
+                    if constexpr (SPLIT) sEL[vc * LDC + t] = from_f32<T>(e - to_f32(eh));
+                }
             }
         }
         __syncthreads();
 
-        // ================= O += P U -> global ;  S = e^{Gn} S + (K e^{Gn-G})^T U =================
+        // ================= U = Tb E  (three-term split product) =================
 #pragma unroll
         for (int i = 0; i < Cfg::NUW; ++i) {
             const int id = wave + i * NW;
             if (id < Cfg::NU_TILES) {
                 const int R = id / NTV, cv = id % NTV;
-                const int kend = ((R + 1) * 16 + KSTEP_C - 1) / KSTEP_C * KSTEP_C;
-                Oacc[i] = tile_mma<T, KPL_C>(Oacc[i], sP, LDC, R * 16, sUT, LDC, cv * 16, 0,
-                                             kend < C ? kend : C, lane);
+                const int kend = min(((R + 1) * 16 + KSTEP_C - 1) / KSTEP_C * KSTEP_C, C);
+                Uacc[i] = tile_mma_f32a<T, KPL_C>(Uacc[i], sA, LDA, R * 16, sEH, sEL, LDC, cv * 16,
+                                                  kend, lane);
+            }
+        }
+        __syncthreads();   // every wave has consumed E before U^T overwrites it
+#pragma unroll
+        for (int i = 0; i < Cfg::NUW; ++i) {
+            const int id = wave + i * NW;
+            if (id < Cfg::NU_TILES) {
+                const int R = id / NTV, cv = id % NTV;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = R * 16 + acc_row(lane, r), vc = cv * 16 + acc_col(lane);
+                    const T uh = from_f32<T>(Uacc[i][r]);
+                    sEH[vc * LDC + t] = uh;
+                    if constexpr (SPLIT) sEL[vc * LDC + t] = from_f32<T>(Uacc[i][r] - to_f32(uh));
+                }
+            }
+        }
+        __syncthreads();
+
+        // ============ O += P U -> global ;  S = e^{Gn} S + (K e^{Gn-G})^T U ============
+#pragma unroll
+        for (int i = 0; i < Cfg::NUW; ++i) {
+            const int id = wave + i * NW;
+            if (id < Cfg::NU_TILES) {
+                const int R = id / NTV, cv = id % NTV;
+                const int kend = min(((R + 1) * 16 + KSTEP_C - 1) / KSTEP_C * KSTEP_C, C);
+                Oacc[i] = tile_mma_f32a<T, KPL_C>(Oacc[i], sPf, LDA, R * 16, sEH, sEL, LDC, cv * 16,
+                                                  kend, lane);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = R * 16 + acc_row(lane, r);
                     if (row < nt)
                         o[(size_t)(c0 + row) * rowV + (size_t)h * DV + v0 + cv * 16 + acc_col(lane)] =
-                            from_f32<T>(Oacc[i][r]);
+                            from_f32<TO>(Oacc[i][r]);
                 }
             }
         }
@@ -431,7 +520,8 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
                 const int rt = id / NTV, ct = id % NTV;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Sacc[i][r] *= sEGn[rt * 16 + acc_row(lane, r)];
-                Sacc[i] = tile_mma<T, KPL_C>(Sacc[i], sK, LDC, rt * 16, sUT, LDC, ct * 16, 0, C, lane);
+                Sacc[i] = tile_mma_split<T, KPL_C>(Sacc[i], sKrH, sKrL, LDC, rt * 16, sEH, sEL, LDC,
+                                                   ct * 16, C, lane);
             }
         }
         store_state_operand();

@@ -1,8 +1,9 @@
-// bf16 instantiations of the chunkwise prefill kernel (bf16 MFMA, fp32 accumulate).
+// bf16-input instantiations of the chunkwise prefill kernel with fp32 output
+// (bf16 MFMA, fp32 accumulate).
 #include "kda_chunk_dispatch.cuh"
 
 namespace kda {
-hipError_t launch_chunk_bf16(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok) {
-    return chunk_detail::dispatch<bf16>(a, s, launch, ok);
+hipError_t launch_chunk_bf16_f32out(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok) {
+    return chunk_detail::dispatch<bf16, float>(a, s, launch, ok);
 }
 }  // namespace kda

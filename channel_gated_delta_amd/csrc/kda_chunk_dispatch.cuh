@@ -8,7 +8,7 @@
 namespace kda {
 namespace chunk_detail {
 
-template <class T, int DK, int BV, int C>
+template <class T, class TO, int DK, int BV, int C>
 hipError_t run(const ChunkArgs &a, hipStream_t s) {
     if constexpr (!ChunkCfg<T, DK, BV, C>::kFits) {
         return hipErrorNotSupported;
@@ -17,10 +17,10 @@ hipError_t run(const ChunkArgs &a, hipStream_t s) {
         const int nslice = a.dv / BV;
         if (units == 0) return hipSuccess;
         const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * nslice);
-        hipLaunchKernelGGL((chunk_kernel<T, DK, BV, C>), dim3(grid), dim3(256), 0, s,
+        hipLaunchKernelGGL((chunk_kernel<T, TO, DK, BV, C>), dim3(grid), dim3(256), 0, s,
                            (const T *)a.q, (const T *)a.k, (const T *)a.v, a.g, a.beta,
                            a.cu_seqlens, a.total_tokens, a.heads, a.dv, a.scale, a.h0, a.hT,
-                           (T *)a.o, units, nslice);
+                           (TO *)a.o, units, nslice);
         return hipGetLastError();
     }
 }
@@ -35,37 +35,37 @@ constexpr int pick_bv(int dv) {
     return 0;
 }
 
-template <class T, int DK, int C>
+template <class T, class TO, int DK, int C>
 hipError_t run_c(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok) {
     const int bv = pick_bv<T, DK, C>(a.dv);
     *ok = bv != 0;
     if (!launch || !*ok) return *ok ? hipSuccess : hipErrorNotSupported;
     switch (bv) {
-        case 64: return run<T, DK, 64, C>(a, s);
-        case 32: return run<T, DK, 32, C>(a, s);
-        default: return run<T, DK, 16, C>(a, s);
+        case 64: return run<T, TO, DK, 64, C>(a, s);
+        case 32: return run<T, TO, DK, 32, C>(a, s);
+        default: return run<T, TO, DK, 16, C>(a, s);
     }
 }
 
-template <class T, int DK>
+template <class T, class TO, int DK>
 hipError_t run_dk(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok) {
     *ok = false;
     hipError_t e = hipErrorNotSupported;
-    if (a.chunk >= 64) { e = run_c<T, DK, 64>(a, s, launch, ok); if (*ok) return e; }
-    if (a.chunk >= 32) { e = run_c<T, DK, 32>(a, s, launch, ok); if (*ok) return e; }
-    if (a.chunk >= 16) { e = run_c<T, DK, 16>(a, s, launch, ok); if (*ok) return e; }
+    if (a.chunk >= 64) { e = run_c<T, TO, DK, 64>(a, s, launch, ok); if (*ok) return e; }
+    if (a.chunk >= 32) { e = run_c<T, TO, DK, 32>(a, s, launch, ok); if (*ok) return e; }
+    if (a.chunk >= 16) { e = run_c<T, TO, DK, 16>(a, s, launch, ok); if (*ok) return e; }
     return hipErrorNotSupported;
 }
 
-template <class T>
+template <class T, class TO>
 hipError_t dispatch(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok) {
     *ok = false;
     if (a.dv != 16 && a.dv != 32 && a.dv != 64 && a.dv != 128) return hipErrorNotSupported;
     switch (a.dk) {
-        case 16: return run_dk<T, 16>(a, s, launch, ok);
-        case 32: return run_dk<T, 32>(a, s, launch, ok);
-        case 64: return run_dk<T, 64>(a, s, launch, ok);
-        case 128: return run_dk<T, 128>(a, s, launch, ok);
+        case 16: return run_dk<T, TO, 16>(a, s, launch, ok);
+        case 32: return run_dk<T, TO, 32>(a, s, launch, ok);
+        case 64: return run_dk<T, TO, 64>(a, s, launch, ok);
+        case 128: return run_dk<T, TO, 128>(a, s, launch, ok);
     }
     return hipErrorNotSupported;
 }

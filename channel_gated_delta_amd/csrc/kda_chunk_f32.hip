@@ -3,6 +3,6 @@
 
 namespace kda {
 hipError_t launch_chunk_f32(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok) {
-    return chunk_detail::dispatch<float>(a, s, launch, ok);
+    return chunk_detail::dispatch<float, float>(a, s, launch, ok);
 }
 }  // namespace kda

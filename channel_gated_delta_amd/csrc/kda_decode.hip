@@ -29,11 +29,11 @@ struct DecodeCfg {
     static_assert(kRowThreads * kRowsPerThread == DK, "row split");
 };
 
-template <class T, int DK, int DV>
+template <class T, class TO, int DK, int DV>
 __global__ __launch_bounds__(256)
 void decode_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                    const float *__restrict__ g, const float *__restrict__ beta,
-                   float *__restrict__ state, float scale, T *__restrict__ o) {
+                   float *__restrict__ state, float scale, TO *__restrict__ o) {
     using Cfg = DecodeCfg<T, DK, DV>;
     constexpr int NT = Cfg::kThreads, RT = Cfg::kRowThreads, RPT = Cfg::kRowsPerThread;
     __shared__ float s_ka[DK];        // a_c * k_c
@@ -100,7 +100,7 @@ void decode_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
         const float b = beta[bh];
         const float e = to_f32(v[(size_t)bh * DV + tid]) - p;
         s_be[tid] = b * e;
-        o[(size_t)bh * DV + tid] = from_f32<T>(scale * (r + b * e * qk));
+        o[(size_t)bh * DV + tid] = from_f32<TO>(scale * (r + b * e * qk));
     }
     __syncthreads();
 
@@ -122,10 +122,16 @@ template <class T, int DK, int DV>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
     const int blocks = a.batch * a.heads;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3(blocks),
-                       dim3(DecodeCfg<T, DK, DV>::kThreads), 0, s,
-                       (const T *)a.q, (const T *)a.k, (const T *)a.v, a.g, a.beta, a.state,
-                       a.scale, (T *)a.o);
+    if (a.out_f32)
+        hipLaunchKernelGGL((decode_kernel<T, float, DK, DV>), dim3(blocks),
+                           dim3(DecodeCfg<T, DK, DV>::kThreads), 0, s,
+                           (const T *)a.q, (const T *)a.k, (const T *)a.v, a.g, a.beta, a.state,
+                           a.scale, (float *)a.o);
+    else
+        hipLaunchKernelGGL((decode_kernel<T, T, DK, DV>), dim3(blocks),
+                           dim3(DecodeCfg<T, DK, DV>::kThreads), 0, s,
+                           (const T *)a.q, (const T *)a.k, (const T *)a.v, a.g, a.beta, a.state,
+                           a.scale, (T *)a.o);
     return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ struct ChunkArgs {
     float scale, gate_lb;
     const float *h0;
     float *hT;
-    void *o;
+    void *o;        // output dtype chosen by the launcher called
 };
 
 struct DecodeArgs {
@@ -39,13 +39,15 @@ struct DecodeArgs {
     int32_t batch, heads, dk, dv;
     float scale;
     void *o;
+    bool out_f32;   // o in fp32 (else in the input dtype)
 };
 
 // Each launcher returns hipSuccess, hipErrorNotSupported for a shape it has no
 // kernel for (checked before anything is enqueued), or the launch error.
 hipError_t launch_short_conv(const ConvArgs &a, bool bf16, hipStream_t s);
 // Chunk prefill per dtype: with launch == false only *ok (shape supported) is set.
-hipError_t launch_chunk_bf16(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok);
+hipError_t launch_chunk_bf16_f32out(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok);
+hipError_t launch_chunk_bf16_bf16out(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok);
 hipError_t launch_chunk_f32(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok);
 hipError_t launch_decode_step(const DecodeArgs &a, bool bf16, hipStream_t s);
 

@@ -22,9 +22,11 @@
  *           contents cannot be checked on the host without a sync; offsets
  *           outside [0, total_tokens] are clamped by the kernels, so a malformed
  *           array yields unspecified values but no out-of-bounds access.
- * Dtypes.   `dtype` names the activation dtype (q, k, v, o, conv input/output,
- *           conv weights and conv state).  Gates (g, beta) and recurrent states
- *           are always fp32.  bf16 results are rounded to nearest even.
+ * Dtypes.   `dtype` names the activation dtype (q, k, v, conv input/output,
+ *           conv weights and conv state); `out_dtype` the read-out o of the
+ *           recurrence (fp32, or bf16 with bf16 inputs).  Gates (g, beta) and
+ *           recurrent states are always fp32.  bf16 results are rounded to
+ *           nearest even.
  * Empty.    With zero tokens (batch 0 for decode) the activation pointers may be
  *           NULL; states are still copied/produced as documented.
  * Errors.   Every call returns a kda_status_t.  Argument checks run on the host
@@ -119,7 +121,7 @@ KDA_API kda_status_t kda_short_conv(const void *x, const void *weight, const voi
  *   initial_state  [num_seqs, num_heads, dk, dv]   fp32 (key index first), or NULL = zeros
  *   final_state    [num_seqs, num_heads, dk, dv]   fp32, or NULL = not written;
  *                  may alias initial_state.
- *   o              [total_tokens, num_heads, dv]   dtype; must not alias any input.
+ *   o              [total_tokens, num_heads, dv]   out_dtype; must not alias any input.
  * scale is the read-out scale (the pages leave the query scale to the caller;
  * dk^-1/2 is the usual choice).  gate_lower_bound is the floor of g promised by
  * the caller ([Walkthrough] 彩蛋: the bounded gate keeps sub-chunk decay products
@@ -127,8 +129,9 @@ KDA_API kda_status_t kda_short_conv(const void *x, const void *weight, const voi
  * promised floor gives unspecified accuracy but no out-of-bounds access.
  * Supported: dk, dv in {16, 32, 64, 128}; chunk_size in {16, 32, 64};
  * |q|, |k| entries below 1e3.  The fp32 dtype computes in fp32 throughout; the
- * bf16 dtype runs its products on bf16 matrix cores with fp32 accumulation and
- * keeps the recurrent state in fp32.  When a shape's working set does not fit
+ * bf16 dtype runs its products on bf16 matrix cores with fp32 accumulation,
+ * keeps the recurrent state in fp32 and uses split (hi + lo) bf16 operands for
+ * the products that feed o and the state directly.  When a shape's working set does not fit
  * in a CU's 160 KiB LDS at the requested chunk_size (fp32 with dk = 128), the
  * kernel runs the next smaller chunk size instead.
  */
@@ -137,7 +140,7 @@ KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, 
                            int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
                            int32_t chunk_size, float scale, float gate_lower_bound,
                            const float *initial_state, float *final_state, void *o,
-                           kda_dtype_t dtype, void *stream);
+                           kda_dtype_t dtype, kda_dtype_t out_dtype, void *stream);
 
 /*
  * kda_decode_step -- one recurrent KDA step for a batch of sequences, updating
@@ -153,13 +156,13 @@ KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, 
  *   g      [batch, num_heads, dk]        fp32 log-decay
  *   beta   [batch, num_heads]            fp32
  *   state  [batch, num_heads, dk, dv]    fp32, read and written IN PLACE
- *   o      [batch, num_heads, dv]        dtype; must not alias any input.
+ *   o      [batch, num_heads, dv]        out_dtype; must not alias any input.
  * Supported: dk, dv in {16, 32, 64, 128}.
  */
 KDA_API kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const float *g,
                              const float *beta, float *state, int32_t batch, int32_t num_heads,
                              int32_t dk, int32_t dv, float scale, void *o, kda_dtype_t dtype,
-                             void *stream);
+                             kda_dtype_t out_dtype, void *stream);
 
 /* Static description of a status code (never NULL). */
 KDA_API const char *kda_status_string(kda_status_t status);

@@ -77,7 +77,16 @@ def oracle_prefill(inp, spec, heads):
 
 
 def assert_parity(name, got, ref, tol):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
     err = oracle.rel_err(got, ref)
     note("  %-28s rel err %.3e (tol %.0e)" % (name, err, tol))
+    if not (np.isfinite(err) and err <= tol):
+        d = np.abs(got - ref)
+        d[~np.isfinite(d)] = np.inf
+        idx = np.unravel_index(int(np.argmax(d)), d.shape)
+        note("  worst element %s: got %r ref %r (rms ref %.3e, nonfinite %d)" %
+             (idx, got[idx], ref[idx], float(np.sqrt(np.mean(ref * ref))),
+              int(np.sum(~np.isfinite(got)))))
     assert np.isfinite(err) and err <= tol, "%s: rel err %.3e > %.0e" % (name, err, tol)
     return err

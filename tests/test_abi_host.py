@@ -55,11 +55,11 @@ def test_status_strings_and_version(lib):
 
 def chunk(lib, **kw):
     a = dict(q=P, k=P, v=P, g=P, beta=P, cu=NULL, N=1, T=64, H=2, dk=128, dv=128, chunk=64,
-             scale=0.1, lb=-5.0, h0=NULL, hT=NULL, o=ctypes.c_void_p(8192), dtype=BF16)
+             scale=0.1, lb=-5.0, h0=NULL, hT=NULL, o=ctypes.c_void_p(8192), dtype=BF16, odt=F32)
     a.update(kw)
     return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"], a["T"],
                              a["H"], a["dk"], a["dv"], a["chunk"], a["scale"], a["lb"], a["h0"],
-                             a["hT"], a["o"], a["dtype"], NULL)
+                             a["hT"], a["o"], a["dtype"], a["odt"], NULL)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -70,6 +70,8 @@ def chunk(lib, **kw):
     (dict(T=-1), kda.KDA_ERR_INVALID_ARG),
     (dict(H=0), kda.KDA_ERR_INVALID_ARG),
     (dict(dtype=7), kda.KDA_ERR_INVALID_ARG),
+    (dict(odt=5), kda.KDA_ERR_INVALID_ARG),
+    (dict(dtype=F32, odt=BF16), kda.KDA_ERR_UNSUPPORTED),
     (dict(scale=float("nan")), kda.KDA_ERR_INVALID_ARG),
     (dict(o=P), kda.KDA_ERR_INVALID_ARG),            # o aliases q
     (dict(lb=0.5), kda.KDA_ERR_INVALID_ARG),
@@ -115,12 +117,14 @@ def test_short_conv_rejects(lib, kw, status):
     (dict(B=-1), kda.KDA_ERR_INVALID_ARG),
     (dict(o=P), kda.KDA_ERR_INVALID_ARG),
     (dict(dk=8), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=F32, odt=BF16), kda.KDA_ERR_UNSUPPORTED),
 ])
 def test_decode_step_rejects(lib, kw, status):
-    a = dict(state=ctypes.c_void_p(12288), B=4, H=2, dk=128, dv=128, o=ctypes.c_void_p(8192))
+    a = dict(state=ctypes.c_void_p(12288), B=4, H=2, dk=128, dv=128, o=ctypes.c_void_p(8192),
+             dtype=BF16, odt=F32)
     a.update(kw)
     assert lib.kda_decode_step(P, P, P, P, P, a["state"], a["B"], a["H"], a["dk"], a["dv"], 0.1,
-                               a["o"], BF16, NULL) == status
+                               a["o"], a["dtype"], a["odt"], NULL) == status
 
 
 def test_binding_refuses_cpu_tensors():

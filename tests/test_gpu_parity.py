@@ -71,9 +71,25 @@ def test_prologue_pipeline_varlen(dtype):
 
 
 @pytest.mark.parametrize("lb,std", [(-8.0, 2.0), (-10.0, 3.0)])
-def test_strong_decay(lb, std):
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_strong_decay(lb, std, dtype):
     """Gate floors below -5 (16-token decay span up to e^-160): finite and accurate."""
-    check_prefill(spec_of([256, 77], H=2, lb=lb, gate_std=std, h0=0.05, seed=int(-lb)))
+    check_prefill(spec_of([256, 77], H=2, lb=lb, gate_std=std, h0=0.05, seed=int(-lb),
+                          dtype=dtype))
+
+
+def test_bf16_output_is_rounded_fp32_output():
+    """With bf16 inputs, a bf16 o is exactly the fp32 o rounded to nearest even."""
+    spec = spec_of([130, 64], H=2, h0=0.05, seed=21)
+    inp = workloads.make_prefill(spec, DEV)
+    o32, h32 = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                             cu_seqlens=inp["cu_seqlens"], initial_state=inp["h0"])
+    o16, h16 = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                             cu_seqlens=inp["cu_seqlens"], initial_state=inp["h0"],
+                             out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(h16, h32)
 
 
 def test_identity_gate_keeps_state():
@@ -211,6 +227,14 @@ def decode_case(B, H, dk, dv, steps, dtype, seed, pairs=None):
     got_o = torch.stack([x[bi, hi] for x in outs], dim=1).reshape(P * steps, 1, dv)
     tol = 2e-2 if dtype == torch.bfloat16 else 1e-4
     assert_parity("decode o", to64(got_o), o, tol)
+    if dtype == torch.bfloat16:   # a bf16 o is the fp32 o rounded once
+        st2 = s0.clone()
+        for t in range(steps):
+            d = ins[t]
+            o16 = kda.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], st2,
+                                  scale=dk ** -0.5, out_dtype=torch.bfloat16)
+            assert torch.equal(o16, outs[t].to(torch.bfloat16))
+        assert torch.equal(st2, state)
     assert_parity("decode state", to64(state[bi, hi]).reshape(P, 1, dk, dv), hT, tol)
     return state
 
