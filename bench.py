@@ -63,9 +63,9 @@ def prefill_step_bytes(T: int, H: int, dk: int, dv: int, N: int, h0: bool) -> fl
     """Algorithmic HBM bytes of one chunk-kernel launch: every tensor once.
 
     per token per head: q, k (bf16) 2*2*dk + v (bf16) 2*dv + g (fp32) 4*dk + beta 4
-    + o (bf16) 2*dv; plus the final state (and the initial state when given).
+    + o (fp32) 4*dv; plus the final state (and the initial state when given).
     """
-    per_tok_head = 2 * dk + 2 * dk + 2 * dv + 4 * dk + 4 + 2 * dv
+    per_tok_head = 2 * dk + 2 * dk + 2 * dv + 4 * dk + 4 + 4 * dv
     states = N * H * dk * dv * 4 * (2 if h0 else 1)
     return float(T * H * per_tok_head + states)
 
@@ -76,8 +76,8 @@ def prologue_bytes(T: int, H: int, d: int) -> float:
 
 
 def decode_step_bytes(B: int, H: int, dk: int, dv: int) -> float:
-    """State read + write (fp32) plus q, k, v, o (bf16), g (fp32), beta per (seq, head)."""
-    return float(B * H * (2 * dk * dv * 4 + 2 * dk * 2 + 2 * dv * 2 + 4 * dk + 4))
+    """State read + write (fp32) plus q, k, v (bf16), g (fp32), beta, o (fp32) per (seq, head)."""
+    return float(B * H * (2 * dk * dv * 4 + 2 * dk * 2 + dv * 2 + 4 * dk + 4 + 4 * dv))
 
 
 def run_prefill(args, torch, kda, workloads):
@@ -91,7 +91,7 @@ def run_prefill(args, torch, kda, workloads):
     qb = torch.empty((T, H, DK), dtype=spec.dtype, device=dev)
     kb = torch.empty_like(qb)
     vb = torch.empty((T, H, DV), dtype=spec.dtype, device=dev)
-    ob = torch.empty((T, H, DV), dtype=spec.dtype, device=dev)
+    ob = torch.empty((T, H, DV), dtype=torch.float32, device=dev)
     hT = torch.empty((N, H, DK, DV), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -134,7 +134,7 @@ def run_decode(torch, kda, workloads, steps=256, warmup=16):
     B, H, DK, DV = spec.batch, spec.heads, spec.dk, spec.dv
     state = workloads.make_decode_state(spec, dev)
     ins = [workloads.make_decode_step(spec, t, dev) for t in range(steps)]
-    o = torch.empty((B, H, DV), dtype=spec.dtype, device=dev)
+    o = torch.empty((B, H, DV), dtype=torch.float32, device=dev)
     scratch = state.clone()
     for t in range(warmup):
         d = ins[t % steps]
@@ -177,9 +177,9 @@ def cpu_baseline(res, workloads):
     h0 = None if inp["h0"] is None else f64(inp["h0"][:, heads])
     oracle.default()
     t0 = time.perf_counter()
-    q = oracle.prologue(xq, wq, n_heads, DK, cu, normalize=True)
-    k = oracle.prologue(xk, wk, n_heads, DK, cu, normalize=True)
-    v = oracle.prologue(xv, wv, n_heads, DV, cu)
+    q = oracle.prologue(xq, wq, n_heads, DK, cu, normalize=True, out_bf16=True)
+    k = oracle.prologue(xk, wk, n_heads, DK, cu, normalize=True, out_bf16=True)
+    v = oracle.prologue(xv, wv, n_heads, DV, cu, out_bf16=True)
     oracle.recurrent(q, k, v, g, beta, cu, spec.read_scale, h0)
     dt = time.perf_counter() - t0
     # tokens/s of the whole workload: the sample covers n_heads of H heads
@@ -230,7 +230,8 @@ def main():
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_step"], 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (fp32 accumulate, split-bf16 products, fp32 state and o)",
         "data": "synthetic (seeded; no weights or datasets)",
         "config": {"workload": spec.name, "batch": N, "seq_len": T, "heads": H, "dk": DK,
                    "dv": DV, "chunk": spec.chunk, "path": "3x short_conv (conv4+SiLU, q/k L2) + "

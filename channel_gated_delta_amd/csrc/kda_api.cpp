@@ -102,8 +102,8 @@ KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, 
     if (o && (o == q || o == k || o == v || o == (const void *)g || o == (const void *)beta))
         return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: o aliases an input");
     if (!(gate_lower_bound <= 0.f)) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: gate bound > 0 or NaN");
-    if (gate_lower_bound < -10.f)
-        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: gate_lower_bound below -10");
+    if (gate_lower_bound < -9.f)
+        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: gate_lower_bound below -9");
     if (!head_dim_ok(dk) || !head_dim_ok(dv))
         return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: dk/dv not in {16,32,64,128}");
     if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64)

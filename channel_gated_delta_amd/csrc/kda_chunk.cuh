@@ -35,12 +35,16 @@
 //
 // Decay numerics ([Walkthrough] 彩蛋: products of retention factors and their
 // reciprocals must stay inside the floating-point range).  The Gram matrices
-// factor e^{G_t - G_i} through 16-token sub-tiles referenced at the tile's
-// middle row m: rows use e^{G_t - G_m}, columns e^{G_m - G_i}, both bounded by
-// e^{8|lb|} (finite for lb >= -10); off-diagonal tile pairs (R, I) scale the
-// column operand by the per-channel boundary factor e^{G_{m_R} - G_{m_I}} <= 1.
-// Every other factor (e^{G_t}, e^{G_n - G_t}, e^{G_n}) is <= 1 and is
-// exponentiated directly.  Exponents are in log2 units (v_exp_f32).
+// factor e^{G_t - G_i} through 16-token sub-tiles.  Diagonal tiles use the
+// tile's middle row m as reference: rows e^{G_t - G_m}, columns e^{G_m - G_i},
+// both within e^{+-8|lb|}; a column factor can only underflow (< e^-87) where
+// the lost term is below e^{-87 + 8|lb|}, negligible for lb >= -9.  Off-diagonal
+// pairs (R, I < R) use the first row s of tile R: rows e^{G_t - G_s} (the middle-
+// referenced row operand times e^{G_m - G_s}, both representable) and columns
+// e^{G_s - G_i} (the middle-referenced column operand of tile I times
+// e^{G_s - G_{m_I}}); both factors are <= 1, so any underflow means a
+// negligible product.  Every other factor (e^{G_t}, e^{G_n - G_t}, e^{G_n}) is
+// <= 1 and is exponentiated directly.  Exponents are in log2 units (v_exp_f32).
 #pragma once
 
 #include <type_traits>
@@ -79,7 +83,7 @@ struct ChunkCfg {
     static constexpr size_t szS = al((size_t)BV * LDK * sizeof(T));      // [BV][DK]
     static constexpr size_t szY = al((size_t)(NTC > 1 ? NTC - 1 : 1) * 256 * 4);
     static constexpr size_t szSmall =
-        al((size_t)(2 * C + (NPAIR > 0 ? NPAIR : 1) * DK + (NTC + 2 + NP) * DK) * 4);
+        al((size_t)(2 * C + (NPAIR > 0 ? NPAIR : 1) * DK + (3 * NTC + 2 + NP) * DK) * 4);
     static constexpr size_t oQ = 0;                    // raw q -> q*Dr -> scale q e^G
     static constexpr size_t oK = oQ + szCK;            // raw k -> k*Dr -> k e^G
     static constexpr size_t oX = oK + szCK;            // k*Dc, then (k e^{Gn-G})^T hi/lo
@@ -200,9 +204,11 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
     float *sY = reinterpret_cast<float *>(smem + Cfg::oY);
     float *sBeta = reinterpret_cast<float *>(smem + Cfg::oSmall);
     float *sPd = sBeta + C;                                            // scale q_t . k_t
-    float *sBnd = sPd + C;                                             // e^{G_mR - G_mI}
+    float *sBnd = sPd + C;                                             // e^{G_sR - G_mI}, I < R
     float *sGm = sBnd + (Cfg::NPAIR > 0 ? Cfg::NPAIR : 1) * DK;        // G at tile middles
-    float *sGl = sGm + NTC * DK;                                       // G at the last row
+    float *sGs = sGm + NTC * DK;                                       // G at tile first rows
+    float *sRsc = sGs + NTC * DK;                                      // e^{G_mR - G_sR}
+    float *sGl = sRsc + NTC * DK;                                      // G at the last row
     float *sEGn = sGl + DK;                                            // e^{G_last}
     float *sTot = sEGn + DK;                                           // part sums of g
 
@@ -314,6 +320,7 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
                 gam[j] += off;
                 const int r = part * RP + j;
                 if ((r & 15) == 8) sGm[(r >> 4) * DK + cc] = gam[j];
+                if ((r & 15) == 0) sGs[(r >> 4) * DK + cc] = gam[j];
                 if (r == C - 1) sGl[cc] = gam[j];
             }
         }
@@ -346,11 +353,13 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
             if (part == 0) {
                 sEGn[cc] = exp2_clamped(gl);
 #pragma unroll
-                for (int R = 1; R < NTC; ++R)
+                for (int R = 1; R < NTC; ++R) {
+                    sRsc[R * DK + cc] = exp2_clamped(sGm[R * DK + cc] - sGs[R * DK + cc]);
 #pragma unroll
                     for (int I = 0; I < R; ++I)
                         sBnd[(R * (R - 1) / 2 + I) * DK + cc] =
-                            exp2_clamped(sGm[R * DK + cc] - sGm[I * DK + cc]);
+                            exp2_clamped(sGs[R * DK + cc] - sGm[I * DK + cc]);
+                }
             }
         }
         __syncthreads();
@@ -361,11 +370,17 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
             f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
             if (I <= R) {
                 const float *bnd = sBnd + (I < R ? (R * (R - 1) / 2 + I) * DK : 0);
+                const float *rsc = sRsc + R * DK;
                 for (int k0 = 0; k0 < DK; k0 += 4 * KPL_DK) {
                     auto ak = load_frag<T, KPL_DK>(sK, LDK, R * 16, k0, lane);
                     auto aq = load_frag<T, KPL_DK>(sQ, LDK, R * 16, k0, lane);
                     auto bc = load_frag<T, KPL_DK>(sX, LDK, I * 16, k0, lane);
-                    if (I < R) scale_frag(bc, bnd + k0 + (lane >> 4) * KPL_DK);
+                    if (I < R) {   // re-reference rows to s_R, columns to s_R
+                        const int kk = k0 + (lane >> 4) * KPL_DK;
+                        scale_frag(ak, rsc + kk);
+                        scale_frag(aq, rsc + kk);
+                        scale_frag(bc, bnd + kk);
+                    }
                     accA = mma(ak, bc, accA);
                     accP = mma(aq, bc, accP);
                 }

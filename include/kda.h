@@ -125,7 +125,7 @@ KDA_API kda_status_t kda_short_conv(const void *x, const void *weight, const voi
  * scale is the read-out scale (the pages leave the query scale to the caller;
  * dk^-1/2 is the usual choice).  gate_lower_bound is the floor of g promised by
  * the caller ([Walkthrough] 彩蛋: the bounded gate keeps sub-chunk decay products
- * inside the floating-point range); it must be in [-10, 0].  g below the
+ * inside the floating-point range); it must be in [-9, 0].  g below the
  * promised floor gives unspecified accuracy but no out-of-bounds access.
  * Supported: dk, dv in {16, 32, 64, 128}; chunk_size in {16, 32, 64};
  * |q|, |k| entries below 1e3.  The fp32 dtype computes in fp32 throughout; the

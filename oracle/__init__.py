@@ -24,7 +24,8 @@ Contents:
 
 * ``short_conv``  (O1a) causal depthwise conv + SiLU with conv cache  -- C, fp64
 * ``l2norm``      (O1b) q/k L2 normalisation                          -- C, fp64
-* ``prologue``    O1a + O1b for one of q, k, v                         -- C, fp64
+* ``round_bf16``  (O1c) rounding of an interface tensor to bf16         -- C, fp64
+* ``prologue``    O1a + O1b (+ O1c) for one of q, k, v                 -- C, fp64
 * ``recurrent``   (O2) token-by-token KDA recurrence                   -- C, fp64
 * ``oracle.chunked.chunked_forward``: an independently derived chunkwise
   form, used only as a brute-force pin of ``recurrent`` on tiny inputs.
@@ -95,6 +96,8 @@ class OracleLib:
             _dp, _dp, _dp, _dp, _dp, _ip, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_double, _dp, _dp, _dp, ctypes.c_int]
         lib.kda_oracle_recurrent.restype = ctypes.c_int
+        lib.kda_oracle_round_bf16.argtypes = [_dp, ctypes.c_int64]
+        lib.kda_oracle_round_bf16.restype = None
         lib.kda_oracle_num_threads.argtypes = []
         lib.kda_oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -135,11 +138,19 @@ class OracleLib:
         self.lib.kda_oracle_l2norm(_ptr(y), rows, D, float(eps))
         return y
 
+    def round_bf16(self, x) -> np.ndarray:
+        """O1c: round to the nearest bf16 value (ties to even)."""
+        y = _f64(x).copy()
+        self.lib.kda_oracle_round_bf16(_ptr(y), y.size)
+        return y
+
     def prologue(self, x, w, H: int, D: int, cu_seqlens=None, state_in=None, bias=None,
-                 normalize: bool = False, eps: float = 1e-6, return_state=False):
+                 normalize: bool = False, eps: float = 1e-6, return_state=False,
+                 out_bf16: bool = False):
         """O1: conv + SiLU, then (q and k only) per-head L2 normalisation.
 
         x: [T, H*D] raw projection; returns [T, H, D] (and the conv history).
+        out_bf16: the result is the pipeline's bf16 interface tensor (O1c).
         """
         out = self.short_conv(x, w, cu_seqlens, state_in, bias, silu=True,
                               return_state=return_state)
@@ -147,6 +158,8 @@ class OracleLib:
         T = y.shape[0]
         if normalize:
             y = self.l2norm(y, D, eps)
+        if out_bf16:
+            y = self.round_bf16(y)
         y = y.reshape(T, H, D)
         return (y, st) if return_state else y
 
@@ -200,6 +213,10 @@ def l2norm(*a, **kw):
 
 def prologue(*a, **kw):
     return default().prologue(*a, **kw)
+
+
+def round_bf16(*a, **kw):
+    return default().round_bf16(*a, **kw)
 
 
 def recurrent(*a, **kw):

@@ -107,6 +107,22 @@ void kda_oracle_l2norm(double *x, int64_t rows, int64_t D, double eps) {
 }
 
 /*
+ * O1c. Rounding to bf16 (8 significant bits, round half to even), in place.
+ *      The pipeline hands q, k, v from the prologue to the recurrence as
+ *      tensors of the activation dtype; with bf16 activations the oracle rounds
+ *      its fp64 prologue result the same way before the recurrence.  Values in
+ *      the bf16 normal range are assumed (|x| >= 2^-126 or 0).
+ */
+void kda_oracle_round_bf16(double *x, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) {
+        if (x[i] == 0.0 || !isfinite(x[i])) continue;
+        int e;
+        const double m = frexp(x[i], &e);          /* x = m * 2^e, 0.5 <= |m| < 1 */
+        x[i] = ldexp(nearbyint(ldexp(m, 8)), e - 8);
+    }
+}
+
+/*
  * O2. The KDA recurrence, one token at a time, in the order the source-code
  *     walkthrough fixes ([Walkthrough] 第三站 forget first because the order
  *     matters; 第四站 read the prediction along k, form the error, write it

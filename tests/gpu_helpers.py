@@ -60,11 +60,14 @@ def oracle_prefill(inp, spec, heads):
         return to64(w.view(H, D, -1)[heads].reshape(len(heads) * D, -1))
 
     if spec.conv:
+        # q, k, v reach the recurrence as tensors of the activation dtype (O1c)
+        rb = spec.dtype == torch.bfloat16
         q = oracle.prologue(chans(inp["q_raw"], DK), wch(inp["w_q"], DK), len(heads), DK, cu,
-                            normalize=True)
+                            normalize=True, out_bf16=rb)
         k = oracle.prologue(chans(inp["k_raw"], DK), wch(inp["w_k"], DK), len(heads), DK, cu,
-                            normalize=True)
-        v = oracle.prologue(chans(inp["v_raw"], DV), wch(inp["w_v"], DV), len(heads), DV, cu)
+                            normalize=True, out_bf16=rb)
+        v = oracle.prologue(chans(inp["v_raw"], DV), wch(inp["w_v"], DV), len(heads), DV, cu,
+                            out_bf16=rb)
     else:
         q = to64(inp["q"][:, heads])
         k = to64(inp["k"][:, heads])

@@ -278,6 +278,22 @@ def pin_l2norm(orc):
     _close(np.linalg.norm(y, axis=-1), np.ones((7, 3)), what="unit length")
 
 
+def pin_round_bf16(orc):
+    """bf16 rounding: ties go to the even neighbour; other values match torch's
+    float32 -> bfloat16 conversion (a library routine) on fp32-representable inputs."""
+    import torch
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 3 * 2.0 ** -9 + 2.0 ** -1,
+                     0.0, 2.0 ** 20 * (1 + 2.0 ** -8)])
+    want = np.array([1.0, 1 + 2.0 ** -6, -1.0, 0.5 + 2.0 ** -7, 0.0, 2.0 ** 20])
+    _close(orc.round_bf16(ties), want, tol=0.0, what="bf16 ties")
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal(5000) * np.exp(rng.uniform(-20, 20, 5000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    got = orc.round_bf16(x.astype(np.float64))
+    assert np.array_equal(got, ref), "bf16 rounding differs from torch on %d values" % int(
+        np.sum(got != ref))
+
+
 def pin_varlen_and_resume(orc):
     """Packed sequences equal separate runs; a split carrying (S, conv history)
     equals the unsplit run."""
@@ -337,6 +353,6 @@ def pin_k3_sizes(orc=None):
 ALL_PINS = [
     pin_unit_key_example, pin_one_dim_example, pin_two_address_example, pin_update_order,
     pin_identity, pin_pure_decay, pin_overwrite, pin_linear_attention, pin_gated_form,
-    pin_chunked_matches_recurrent, pin_causality, pin_conv_library, pin_l2norm,
+    pin_chunked_matches_recurrent, pin_causality, pin_conv_library, pin_l2norm, pin_round_bf16,
     pin_varlen_and_resume, pin_value_columns_independent, pin_k3_sizes,
 ]

@@ -76,7 +76,7 @@ def chunk(lib, **kw):
     (dict(o=P), kda.KDA_ERR_INVALID_ARG),            # o aliases q
     (dict(lb=0.5), kda.KDA_ERR_INVALID_ARG),
     (dict(lb=float("nan")), kda.KDA_ERR_INVALID_ARG),
-    (dict(lb=-11.0), kda.KDA_ERR_UNSUPPORTED),
+    (dict(lb=-9.5), kda.KDA_ERR_UNSUPPORTED),
     (dict(dk=48), kda.KDA_ERR_UNSUPPORTED),
     (dict(dv=256), kda.KDA_ERR_UNSUPPORTED),
     (dict(chunk=128), kda.KDA_ERR_UNSUPPORTED),

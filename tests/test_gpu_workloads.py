@@ -1,0 +1,97 @@
+"""The five workloads at full size, HIP path vs the fp64 oracle (needs an MI355X).
+
+The GPU runs every head at the full shape, in the launch configuration that
+bench.py times; the oracle recomputes a sample of heads (or of (sequence, head)
+pairs for decode) from the same seeded inputs, one by one.  Every other output
+is checked for finiteness.  Bar: max|gpu - oracle| / rms(oracle) <= 2e-2 (bf16
+inputs) or 1e-4 (fp32 inputs) on outputs and final states.
+"""
+import numpy as np
+import pytest
+import torch
+
+import channel_gated_delta_amd as kda
+import oracle
+from channel_gated_delta_amd import workloads
+from gpu_helpers import assert_parity, gpu_prefill, note, oracle_prefill, to64, tol_for
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run_prefill_workload(name, heads):
+    spec = workloads.standard_specs()[name]
+    note("workload %s: %d tokens, sampled heads %s" % (spec.name, spec.total_tokens, heads))
+    inp = workloads.make_prefill(spec, DEV)
+    got = gpu_prefill(inp, spec)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(got["o"]).all()) and bool(torch.isfinite(got["hT"]).all())
+    go = to64(got["o"][:, heads])
+    gh = to64(got["hT"][:, heads])
+    del got
+    ref = oracle_prefill(inp, spec, heads)
+    tol = tol_for(spec.dtype)
+    assert_parity("o (sampled heads)", go, ref["o"], tol)
+    assert_parity("final state (sampled heads)", gh, ref["hT"], tol)
+    return spec
+
+
+def test_tiny_fp32_workload_full():
+    """B=1, H=1, T=64, d=16, chunk 16, fp32: every output against the oracle."""
+    run_prefill_workload("tiny_fp32", [0])
+
+
+@pytest.mark.timeout(600)
+def test_prefill_workload():
+    """B=1, T=4096, H=96, d=128, chunk 64, bf16, conv4+SiLU+L2 prologue, zero h0."""
+    run_prefill_workload("prefill", [0, 41, 95])
+
+
+@pytest.mark.timeout(600)
+def test_varlen_workload():
+    """8 packed sequences (32768 tokens), random h0 per sequence, conv reset per sequence."""
+    run_prefill_workload("varlen", [7, 64])
+
+
+@pytest.mark.timeout(900)
+def test_long_workload():
+    """B=1, T=131072, H=96, g = -8 sigmoid(N(0, 2)); oracle over the whole sequence."""
+    run_prefill_workload("long", [3, 90])
+
+
+@pytest.mark.timeout(600)
+def test_decode_workload():
+    """64 sequences x 96 heads, 256 in-place steps; sampled (sequence, head) pairs."""
+    spec = workloads.standard_specs()["decode"]
+    B, H, DK, DV, steps = spec.batch, spec.heads, spec.dk, spec.dv, spec.steps
+    pairs = [(0, 0), (5, 17), (31, 48), (40, 95), (63, 7), (63, 95)]
+    note("decode workload: %d x %d heads, %d steps, pairs %s" % (B, H, steps, pairs))
+    state = workloads.make_decode_state(spec, DEV)
+    bi = torch.tensor([p[0] for p in pairs], device=DEV)
+    hi = torch.tensor([p[1] for p in pairs], device=DEV)
+    s0 = state[bi, hi].clone()
+    o = torch.empty((B, H, DV), dtype=torch.float32, device=DEV)
+    keep = {key: [] for key in ("q", "k", "v", "g", "beta")}
+    outs = []
+    for t in range(steps):
+        d = workloads.make_decode_step(spec, t, DEV)
+        kda.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, out=o)
+        outs.append(o[bi, hi].clone())
+        for key in keep:
+            keep[key].append(d[key][bi, hi])
+        assert bool(torch.isfinite(o).all())
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(state).all())
+    P = len(pairs)
+
+    def seq(key):
+        x = torch.stack(keep[key], dim=1)          # [P, steps, ...]
+        return to64(x.reshape(P * steps, 1, *x.shape[2:]))
+
+    ro, rh = oracle.recurrent(seq("q"), seq("k"), seq("v"), seq("g"),
+                              seq("beta").reshape(P * steps, 1), np.arange(P + 1) * steps,
+                              DK ** -0.5, to64(s0).reshape(P, 1, DK, DV))
+    go = to64(torch.stack(outs, dim=1).reshape(P * steps, 1, DV))
+    assert_parity("decode o (sampled pairs)", go, ro, 2e-2)
+    assert_parity("decode state (sampled pairs)", to64(state[bi, hi]).reshape(P, 1, DK, DV), rh,
+                  2e-2)

@@ -51,6 +51,8 @@ MUTANTS = {
     "silu_wrong": [("if (silu) acc = acc / (1.0 + exp(-acc));", "if (silu) acc = acc / (1.0 + exp(acc));")],
     "l2_no_sqrt": [("const double inv = 1.0 / sqrt(ss + eps);", "const double inv = 1.0 / (ss + eps);")],
     "bias_dropped": [("double acc = bias ? bias[c] : 0.0;", "double acc = 0.0;")],
+    "bf16_truncates": [("x[i] = ldexp(nearbyint(ldexp(m, 8)), e - 8);", "x[i] = ldexp(trunc(ldexp(m, 8)), e - 8);")],
+    "bf16_round_half_up": [("x[i] = ldexp(nearbyint(ldexp(m, 8)), e - 8);", "x[i] = ldexp(round(ldexp(m, 8)), e - 8);")],
 }
 
 
