@@ -28,10 +28,16 @@
 // ~10x the rms), so a single bf16 rounding of a product that feeds o or S
 // directly already costs ~2^-9 * 10 of the rms.  Those products therefore use
 // split operands x = hi + lo (both bf16, |lo| <= 2^-9 |x|) and the three-term
-// product hi*hi + hi*lo + lo*hi (~2^-16 relative): Tb (V - Kd S), P U and
-// Kr^T U.  The Gram matrices stay single bf16 products except the diagonal of
-// P (the current token's own term scale q_t . k_t, no decay), which is
-// recomputed exactly in fp32.  S, Qd and Kd are single bf16 operands.
+// product hi*hi + hi*lo + lo*hi (~2^-16 relative): the Gram matrix P, Tb (V -
+// Kd S), P U and Kr^T U.  The diagonal of P (the current token's own term
+// scale q_t . k_t, no decay) is recomputed exactly in fp32.  A, S, Qd and Kd
+// are single bf16 operands (their rounding reaches o only through products
+// that the tests show to stay well inside the tolerance).
+//
+// Latency.  The inputs of chunk i+1 (q, k, v vectors, g, beta) are loaded into
+// registers while chunk i is computed, with row indices clamped into the
+// sequence so every load is unconditional; rows past the end are zeroed when
+// the registers are written to LDS.
 //
 // Decay numerics ([Walkthrough] 彩蛋: products of retention factors and their
 // reciprocals must stay inside the floating-point range).  The Gram matrices
@@ -84,18 +90,30 @@ struct ChunkCfg {
     static constexpr size_t szY = al((size_t)(NTC > 1 ? NTC - 1 : 1) * 256 * 4);
     static constexpr size_t szSmall =
         al((size_t)(2 * C + (NPAIR > 0 ? NPAIR : 1) * DK + (3 * NTC + 2 + NP) * DK) * 4);
-    static constexpr size_t oQ = 0;                    // raw q -> q*Dr -> scale q e^G
+    static constexpr size_t oQ = 0;                    // raw q -> q*Dr (hi) -> scale q e^G
     static constexpr size_t oK = oQ + szCK;            // raw k -> k*Dr -> k e^G
-    static constexpr size_t oX = oK + szCK;            // k*Dc, then (k e^{Gn-G})^T hi/lo
-    static constexpr size_t oV = oX + mx(szCK, NSPLIT * szKC);
+    static constexpr size_t oE = oK + szCK;            // q*Dr lo, then (V - Kd S)^T and U^T hi/lo
+    static constexpr size_t oX = oE + mx(kSplit ? szCK : 0, NSPLIT * szVC);
+                                                       // k*Dc hi/lo, then (k e^{Gn-G})^T hi/lo
+    static constexpr size_t oV = oX + mx(NSPLIT * szCK, NSPLIT * szKC);
     static constexpr size_t oA = oV + szVC;            // A -> T diag(beta)   (fp32)
     static constexpr size_t oP = oA + szCC;            // scale * P           (fp32)
-    static constexpr size_t oE = oP + szCC;            // (V - Kd S)^T hi/lo, then U^T hi/lo
-    static constexpr size_t oS = oE + NSPLIT * szVC;   // S^T operand copy
+    static constexpr size_t oS = oP + szCC;            // S^T operand copy
     static constexpr size_t oY = oS + szS;
     static constexpr size_t oSmall = oY + szY;
     static constexpr size_t kLds = oSmall + szSmall;
     static constexpr bool kFits = kLds <= 160 * 1024;
+    // load vectors per thread and chunk
+    static constexpr int LPR = DK / VEC;                        // 16-byte vectors per q/k row
+    static constexpr int NQV = (C * LPR + NT - 1) / NT;
+    static constexpr int NVV = (C * (BV / VEC) + NT - 1) / NT;
+    // Two workgroups per CU where both the LDS and the 256-register budget of a
+    // wave at that occupancy hold (wider state slices spill at two).
+#ifndef KDA_CHUNK_MIN_WG
+    static constexpr int kMinWg = (kLds <= 80 * 1024 && DK * BV <= 2048) ? 2 : 1;
+#else
+    static constexpr int kMinWg = KDA_CHUNK_MIN_WG;
+#endif
 };
 
 // Packed-sequence offset i clamped to [0, total]; cu == NULL is one sequence.
@@ -112,6 +130,19 @@ __device__ __forceinline__ void scale_frag(bf16x4 &f, const float *s) {
 __device__ __forceinline__ void scale_frag(bf16x8 &f, const float *s) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = (bf16)((float)f[e] * s[e]);
+}
+
+// (hi + lo) * s re-split into a new (hi, lo) pair, in fp32.
+template <class F>
+__device__ __forceinline__ void rescale_split(F &hi, F &lo, const float *s) {
+    constexpr int n = sizeof(F) / sizeof(bf16);
+#pragma unroll
+    for (int e = 0; e < n; ++e) {
+        const float x = ((float)hi[e] + (float)lo[e]) * s[e];
+        const bf16 h = (bf16)x;
+        hi[e] = h;
+        lo[e] = (bf16)(x - (float)h);
+    }
 }
 
 // A-operand fragment read from an fp32 LDS matrix [rows][ld] and split into
@@ -175,7 +206,7 @@ __device__ __forceinline__ f32x4 tile_mma_split(f32x4 acc, const T *Ah, const T 
 }
 
 template <class T, class TO, int DK, int BV, int C>
-__global__ __launch_bounds__(256, 1)
+__global__ __launch_bounds__(256, (ChunkCfg<T, DK, BV, C>::kMinWg))
 void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                   const float *__restrict__ g, const float *__restrict__ beta,
                   const int32_t *__restrict__ cu_seqlens, int64_t total, int H, int DV,
@@ -190,9 +221,11 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
     typedef typename Vec16<T>::type VT;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::kLds];
-    T *sQ = reinterpret_cast<T *>(smem + Cfg::oQ);
+    T *sQ = reinterpret_cast<T *>(smem + Cfg::oQ);                    // q*Dr hi
+    T *sQL = reinterpret_cast<T *>(smem + Cfg::oE);                   // q*Dr lo
     T *sK = reinterpret_cast<T *>(smem + Cfg::oK);
-    T *sX = reinterpret_cast<T *>(smem + Cfg::oX);                    // k*Dc (Gram columns)
+    T *sX = reinterpret_cast<T *>(smem + Cfg::oX);                    // k*Dc hi (Gram columns)
+    T *sXL = reinterpret_cast<T *>(smem + Cfg::oX + (SPLIT ? Cfg::szCK : 0));  // k*Dc lo
     T *sKrH = reinterpret_cast<T *>(smem + Cfg::oX);                  // (k e^{Gn-G})^T hi
     T *sKrL = reinterpret_cast<T *>(smem + Cfg::oX + (SPLIT ? Cfg::szKC : 0));
     T *sVT = reinterpret_cast<T *>(smem + Cfg::oV);                   // V^T slice
@@ -258,21 +291,50 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
 
     // channel-owner mapping used for the decay factors: channel c, tokens [part*RP, +RP)
     const int cc = tid % DK, part = tid / DK;
+    constexpr int LPR = Cfg::LPR, NQV = Cfg::NQV, NVV = Cfg::NVV, VPR = BV / VEC;
+
+    // ---- registers holding the next chunk's inputs (rows clamped into the sequence)
+    VT pq[NQV], pk[NQV], pv[NVV];
+    float pg[RP], pb = 0.f;
+    auto issue_loads = [&](int64_t cs) {
+        const int last = (int)min((int64_t)C, eos - cs) - 1;
+#pragma unroll
+        for (int j = 0; j < NQV; ++j) {
+            const int idx = tid + j * NT;
+            if (C * LPR % NT == 0 || idx < C * LPR) {
+                const int r = min(idx / LPR, last), cv = idx % LPR;
+                const size_t off = (size_t)(cs + r) * rowQK + (size_t)h * DK + cv * VEC;
+                pq[j] = *reinterpret_cast<const VT *>(q + off);
+                pk[j] = *reinterpret_cast<const VT *>(k + off);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) {
+            const int idx = tid + j * NT;
+            if (C * VPR % NT == 0 || idx < C * VPR) {
+                const int r = min(idx / VPR, last), cv = idx % VPR;
+                pv[j] = *reinterpret_cast<const VT *>(v + (size_t)(cs + r) * rowV + (size_t)h * DV +
+                                                      v0 + cv * VEC);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RP; ++j)
+            pg[j] = g[(size_t)(cs + min(part * RP + j, last)) * rowQK + (size_t)h * DK + cc];
+        if (tid < C) pb = beta[(size_t)(cs + min(tid, last)) * H + h];
+    };
+    if (bos < eos) issue_loads(bos);
 
     for (int64_t c0 = bos; c0 < eos; c0 += C) {
         const int nt = (int)min((int64_t)C, eos - c0);
 
-        // ================= L: load the chunk (rows >= nt are zero) =================
-        {
-            constexpr int LPR = DK / VEC;   // lanes per row (power of two <= 32)
-            for (int idx = tid; idx < C * LPR; idx += NT) {
+        // ================= L: registers -> LDS (rows >= nt are zero) =================
+#pragma unroll
+        for (int j = 0; j < NQV; ++j) {
+            const int idx = tid + j * NT;
+            if (C * LPR % NT == 0 || idx < C * LPR) {
                 const int r = idx / LPR, cv = idx % LPR;
-                VT qv = VT{}, kv = VT{};
-                if (r < nt) {
-                    const size_t off = (size_t)(c0 + r) * rowQK + (size_t)h * DK + cv * VEC;
-                    qv = *reinterpret_cast<const VT *>(q + off);
-                    kv = *reinterpret_cast<const VT *>(k + off);
-                }
+                const VT qv = r < nt ? pq[j] : VT{};
+                const VT kv = r < nt ? pk[j] : VT{};
                 *reinterpret_cast<VT *>(sQ + r * LDK + cv * VEC) = qv;
                 *reinterpret_cast<VT *>(sK + r * LDK + cv * VEC) = kv;
                 // exact diagonal of P: scale * q_r . k_r (products of bf16 are exact in fp32)
@@ -283,34 +345,31 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
                 if (cv == 0) sPd[r] = scale * dot;
             }
         }
-        for (int idx = tid; idx < C * (BV / VEC); idx += NT) {
-            const int r = idx / (BV / VEC), cv = idx % (BV / VEC);
-            VT vv = VT{};
-            if (r < nt)
-                vv = *reinterpret_cast<const VT *>(v + (size_t)(c0 + r) * rowV + (size_t)h * DV +
-                                                   v0 + cv * VEC);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) sVT[(cv * VEC + e) * LDC + r] = vv[e];
+        for (int j = 0; j < NVV; ++j) {
+            const int idx = tid + j * NT;
+            if (C * VPR % NT == 0 || idx < C * VPR) {
+                const int r = idx / VPR, cv = idx % VPR;
+                const VT vv = r < nt ? pv[j] : VT{};
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) sVT[(cv * VEC + e) * LDC + r] = vv[e];
+            }
         }
-        if (tid < C) sBeta[tid] = tid < nt ? beta[(size_t)(c0 + tid) * H + h] : 0.f;
+        if (tid < C) sBeta[tid] = tid < nt ? pb : 0.f;
 
         // cumulative log2-decay of channel cc over this thread's tokens (registers)
         float gam[RP];
         {
-            float gv[RP];
-#pragma unroll
-            for (int j = 0; j < RP; ++j) {
-                const int r = part * RP + j;
-                gv[j] = r < nt ? g[(size_t)(c0 + r) * rowQK + (size_t)h * DK + cc] : 0.f;
-            }
             float acc = 0.f;
 #pragma unroll
             for (int j = 0; j < RP; ++j) {
-                acc += gv[j] * kLog2e;
+                acc += (part * RP + j < nt ? pg[j] : 0.f) * kLog2e;
                 gam[j] = acc;
             }
             sTot[part * DK + cc] = acc;
         }
+        // the next chunk's loads fly while this chunk is computed
+        if (c0 + C < eos) issue_loads(c0 + C);
         __syncthreads();
         {
             float off = 0.f;
@@ -327,31 +386,31 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
         __syncthreads();
 
         // ================= F: decay factors =================
-        // Gram operands to LDS: q e^{G_t-G_m}, k e^{G_t-G_m}, k e^{G_m-G_t} (m = middle
-        // row of t's 16-token tile).  Chunk-level operands stay in registers until the
-        // Gram products are done: scale q e^{G_t}, k e^{G_t}, k e^{G_n-G_t} (hi, lo).
-        T rQd[RP], rKd[RP], rKrH[RP], rKrL[RP];
+        // Gram operands to LDS: q e^{G_t-G_m} (hi, lo), k e^{G_t-G_m}, k e^{G_m-G_t} (hi, lo)
+        // (m = middle row of t's 16-token tile).  Raw q, k stay in registers for the
+        // chunk-level operands, formed after the Gram products.
+        T rq[RP], rk[RP];
         {
-            const float gl = sGl[cc];
 #pragma unroll
             for (int j = 0; j < RP; ++j) {
                 const int r = part * RP + j;
-                const float gt = gam[j];
-                const float d = gt - sGm[(r >> 4) * DK + cc];
+                const float d = gam[j] - sGm[(r >> 4) * DK + cc];
                 const float dr = exp2_clamped(d), dc = exp2_clamped(-d);
-                const float eg = exp2_clamped(gt), egr = exp2_clamped(gl - gt);
-                const float qf = to_f32(sQ[r * LDK + cc]), kf = to_f32(sK[r * LDK + cc]);
-                sQ[r * LDK + cc] = from_f32<T>(qf * dr);
+                rq[j] = sQ[r * LDK + cc];
+                rk[j] = sK[r * LDK + cc];
+                const float qf = to_f32(rq[j]), kf = to_f32(rk[j]);
+                const float qd = qf * dr, kc = kf * dc;
+                const T qdh = from_f32<T>(qd), kch = from_f32<T>(kc);
+                sQ[r * LDK + cc] = qdh;
                 sK[r * LDK + cc] = from_f32<T>(kf * dr);
-                sX[r * LDK + cc] = from_f32<T>(kf * dc);
-                rQd[j] = from_f32<T>(qf * eg * scale);
-                rKd[j] = from_f32<T>(kf * eg);
-                const float kr = kf * egr;
-                rKrH[j] = from_f32<T>(kr);
-                rKrL[j] = from_f32<T>(kr - to_f32(rKrH[j]));
+                sX[r * LDK + cc] = kch;
+                if constexpr (SPLIT) {
+                    sQL[r * LDK + cc] = from_f32<T>(qd - to_f32(qdh));
+                    sXL[r * LDK + cc] = from_f32<T>(kc - to_f32(kch));
+                }
             }
             if (part == 0) {
-                sEGn[cc] = exp2_clamped(gl);
+                sEGn[cc] = exp2_clamped(sGl[cc]);
 #pragma unroll
                 for (int R = 1; R < NTC; ++R) {
                     sRsc[R * DK + cc] = exp2_clamped(sGm[R * DK + cc] - sGs[R * DK + cc]);
@@ -373,16 +432,29 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
                 const float *rsc = sRsc + R * DK;
                 for (int k0 = 0; k0 < DK; k0 += 4 * KPL_DK) {
                     auto ak = load_frag<T, KPL_DK>(sK, LDK, R * 16, k0, lane);
-                    auto aq = load_frag<T, KPL_DK>(sQ, LDK, R * 16, k0, lane);
-                    auto bc = load_frag<T, KPL_DK>(sX, LDK, I * 16, k0, lane);
-                    if (I < R) {   // re-reference rows to s_R, columns to s_R
-                        const int kk = k0 + (lane >> 4) * KPL_DK;
-                        scale_frag(ak, rsc + kk);
-                        scale_frag(aq, rsc + kk);
-                        scale_frag(bc, bnd + kk);
+                    auto qh = load_frag<T, KPL_DK>(sQ, LDK, R * 16, k0, lane);
+                    auto ch = load_frag<T, KPL_DK>(sX, LDK, I * 16, k0, lane);
+                    if constexpr (SPLIT) {
+                        auto ql = load_frag<T, KPL_DK>(sQL, LDK, R * 16, k0, lane);
+                        auto cl = load_frag<T, KPL_DK>(sXL, LDK, I * 16, k0, lane);
+                        if (I < R) {   // re-reference rows and columns to s_R
+                            const int kk = k0 + (lane >> 4) * KPL_DK;
+                            scale_frag(ak, rsc + kk);
+                            rescale_split(qh, ql, rsc + kk);
+                            rescale_split(ch, cl, bnd + kk);
+                        }
+                        accP = mma(qh, cl, accP);
+                        accP = mma(ql, ch, accP);
+                    } else {
+                        if (I < R) {
+                            const int kk = k0 + (lane >> 4) * KPL_DK;
+                            scale_frag(ak, rsc + kk);
+                            scale_frag(qh, rsc + kk);
+                            scale_frag(ch, bnd + kk);
+                        }
                     }
-                    accA = mma(ak, bc, accA);
-                    accP = mma(aq, bc, accP);
+                    accA = mma(ak, ch, accA);
+                    accP = mma(qh, ch, accP);
                 }
             }
 #pragma unroll
@@ -395,13 +467,21 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
         __syncthreads();
 
         // ================= X: chunk-level operands; inverse diagonal blocks =================
+        // scale q e^{G_t} over q*Dr, k e^{G_t} over k*Dr, (k e^{G_n-G_t})^T hi/lo over k*Dc
+        {
+            const float gl = sGl[cc];
 #pragma unroll
-        for (int j = 0; j < RP; ++j) {
-            const int r = part * RP + j;
-            sQ[r * LDK + cc] = rQd[j];
-            sK[r * LDK + cc] = rKd[j];
-            sKrH[cc * LDC + r] = rKrH[j];
-            if constexpr (SPLIT) sKrL[cc * LDC + r] = rKrL[j];
+            for (int j = 0; j < RP; ++j) {
+                const int r = part * RP + j;
+                const float eg = exp2_clamped(gam[j]), egr = exp2_clamped(gl - gam[j]);
+                const float qf = to_f32(rq[j]), kf = to_f32(rk[j]);
+                sQ[r * LDK + cc] = from_f32<T>(qf * eg * scale);
+                sK[r * LDK + cc] = from_f32<T>(kf * eg);
+                const float kr = kf * egr;
+                const T krh = from_f32<T>(kr);
+                sKrH[cc * LDC + r] = krh;
+                if constexpr (SPLIT) sKrL[cc * LDC + r] = from_f32<T>(kr - to_f32(krh));
+            }
         }
         // diagonal 16x16 blocks of (I + diag(beta) A)^{-1}: lane i builds column i
         for (int R = wave; R < NTC; R += NW) {

@@ -25,13 +25,23 @@ hipError_t run(const ChunkArgs &a, hipStream_t s) {
     }
 }
 
-// Widest value slice that divides dv and fits in LDS, trying the requested chunk
-// first and then smaller ones (the result does not depend on the chunk size).
+// Value-slice width.  Each slice repeats the key-side work (decay factors, Gram
+// matrices, inverse), so wider slices waste less; narrower slices give more
+// workgroups to fill 256 CUs (96 heads x 4 slices of 32 = 384).  32 columns when
+// dv allows it and it fits, else 64, else 16.
+template <class T, int DK, int BV, int C>
+constexpr bool fits(int dv, size_t limit) {
+    return dv % BV == 0 && ChunkCfg<T, DK, BV, C>::kLds <= limit;
+}
 template <class T, int DK, int C>
 constexpr int pick_bv(int dv) {
-    if (dv % 64 == 0 && ChunkCfg<T, DK, 64, C>::kFits) return 64;
-    if (dv % 32 == 0 && ChunkCfg<T, DK, 32, C>::kFits) return 32;
-    if (dv % 16 == 0 && ChunkCfg<T, DK, 16, C>::kFits) return 16;
+#ifdef KDA_CHUNK_BV
+    if (dv % KDA_CHUNK_BV == 0 && ChunkCfg<T, DK, KDA_CHUNK_BV, C>::kFits) return KDA_CHUNK_BV;
+#endif
+    const size_t limit = (size_t)160 * 1024;
+    if (fits<T, DK, 32, C>(dv, limit)) return 32;
+    if (fits<T, DK, 64, C>(dv, limit)) return 64;
+    if (fits<T, DK, 16, C>(dv, limit)) return 16;
     return 0;
 }
 
@@ -47,11 +57,19 @@ hipError_t run_c(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok) {
     }
 }
 
+// Internal chunk: the requested size or smaller.  The bf16 path prefers 32 tokens:
+// its split products make the intra-chunk work per token grow with the chunk,
+// and the smaller working set fits two workgroups per CU.
 template <class T, class TO, int DK>
 hipError_t run_dk(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok) {
     *ok = false;
     hipError_t e = hipErrorNotSupported;
-    if (a.chunk >= 64) { e = run_c<T, TO, DK, 64>(a, s, launch, ok); if (*ok) return e; }
+#ifdef KDA_CHUNK_PREFER32
+    constexpr bool kPrefer32 = KDA_CHUNK_PREFER32;
+#else
+    constexpr bool kPrefer32 = std::is_same<T, bf16>::value;
+#endif
+    if (a.chunk >= 64 && !kPrefer32) { e = run_c<T, TO, DK, 64>(a, s, launch, ok); if (*ok) return e; }
     if (a.chunk >= 32) { e = run_c<T, TO, DK, 32>(a, s, launch, ok); if (*ok) return e; }
     if (a.chunk >= 16) { e = run_c<T, TO, DK, 16>(a, s, launch, ok); if (*ok) return e; }
     return hipErrorNotSupported;
