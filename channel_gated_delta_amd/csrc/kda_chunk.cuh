@@ -16,28 +16,23 @@
 //   S    = diag(e^{G_n}) S0 + (K * e^{G_n - G})^T U
 //
 // Work decomposition.  One workgroup (4 waves) owns one (sequence, head, value
-// slice of BV columns) and walks the chunks of its sequence; value columns of S
-// evolve independently, so slicing multiplies the parallelism of a head.  The
-// fp32 state slice lives in MFMA accumulator registers for the whole sequence
-// and is mirrored into LDS in the operand dtype once per chunk.  Products run
-// on 16x16 MFMA tiles (bf16 in / fp32 accumulate; fp32 MFMA for fp32 inputs);
-// the unit-lower-triangular inverse is done in fp32 (16x16 forward substitution
-// per diagonal block, then blockwise fp32 MFMA merges).
+// slice of BV columns) and walks the chunks of its sequence.  Wave w < BV/16
+// owns the 16 state columns [16w, 16w+16) of the slice: its part of the fp32
+// state lives in MFMA accumulator registers for the whole sequence, and the
+// whole state-dependent chain of a chunk (V - Kd S, Tb E, Qd S + P U, the state
+// update) runs inside that wave from registers -- an accumulator tile doubles
+// as the B operand of the next product when the A fragment is read with the
+// matching k order -- so the chain needs no LDS traffic and no barrier.  The
+// state-independent part (decay factors, Gram matrices, the unit-lower-
+// triangular inverse) is shared by the four waves through LDS.
 //
-// Precision of the bf16 path.  The outputs are heavy-tailed (the largest |o| is
-// ~10x the rms), so a single bf16 rounding of a product that feeds o or S
-// directly already costs ~2^-9 * 10 of the rms.  Those products therefore use
-// split operands x = hi + lo (both bf16, |lo| <= 2^-9 |x|) and the three-term
-// product hi*hi + hi*lo + lo*hi (~2^-16 relative): the Gram matrix P, Tb (V -
-// Kd S), P U and Kr^T U.  The diagonal of P (the current token's own term
-// scale q_t . k_t, no decay) is recomputed exactly in fp32.  A, S, Qd and Kd
-// are single bf16 operands (their rounding reaches o only through products
-// that the tests show to stay well inside the tolerance).
-//
-// Latency.  The inputs of chunk i+1 (q, k, v vectors, g, beta) are loaded into
-// registers while chunk i is computed, with row indices clamped into the
-// sequence so every load is unconditional; rows past the end are zeroed when
-// the registers are written to LDS.
+// Precision.  The outputs are heavy-tailed (the largest |o| is 10-30x the rms),
+// so one bf16 rounding of a product feeding o or S already costs ~2^-9 * 30 of
+// the rms.  With bf16 inputs every product therefore uses split operands
+// x = hi + lo (both bf16, |lo| <= 2^-9 |x|) and the three-term product
+// hi*hi + hi*lo + lo*hi (~2^-16 relative); the diagonal of P (the current
+// token's own term scale q_t . k_t, no decay) is recomputed exactly in fp32.
+// With fp32 inputs the products run on fp32 MFMA.
 //
 // Decay numerics ([Walkthrough] 彩蛋: products of retention factors and their
 // reciprocals must stay inside the floating-point range).  The Gram matrices
@@ -46,11 +41,16 @@
 // both within e^{+-8|lb|}; a column factor can only underflow (< e^-87) where
 // the lost term is below e^{-87 + 8|lb|}, negligible for lb >= -9.  Off-diagonal
 // pairs (R, I < R) use the first row s of tile R: rows e^{G_t - G_s} (the middle-
-// referenced row operand times e^{G_m - G_s}, both representable) and columns
-// e^{G_s - G_i} (the middle-referenced column operand of tile I times
-// e^{G_s - G_{m_I}}); both factors are <= 1, so any underflow means a
-// negligible product.  Every other factor (e^{G_t}, e^{G_n - G_t}, e^{G_n}) is
-// <= 1 and is exponentiated directly.  Exponents are in log2 units (v_exp_f32).
+// referenced row operand times e^{G_m - G_s}) and columns e^{G_s - G_i} (the
+// middle-referenced column operand of tile I times e^{G_s - G_{m_I}}); both
+// factors are <= 1, so any underflow means a negligible product.  Every other
+// factor (e^{G_t}, e^{G_n - G_t}, e^{G_n}) is <= 1 and is exponentiated
+// directly.  Exponents are in log2 units (v_exp_f32).
+//
+// Latency.  The inputs of chunk i+1 (q, k vectors, V in accumulator layout, g,
+// beta) are loaded into registers while chunk i is computed, with row indices
+// clamped into the sequence so every load is unconditional; rows past the end
+// are zeroed when the registers are consumed.
 #pragma once
 
 #include <type_traits>
@@ -65,52 +65,43 @@ struct ChunkCfg {
     static constexpr bool kSplit = std::is_same<T, bf16>::value;
     static constexpr int NSPLIT = kSplit ? 2 : 1;
     static constexpr int NW = 4, NT = NW * kWave;
-    static constexpr int NTC = C / 16, NTK = DK / 16, NTV = BV / 16;
+    static constexpr int NTC = C / 16, NTK = DK / 16, NCW = BV / 16;
     static constexpr int VEC = 16 / (int)sizeof(T);             // elements per 16-byte vector
     static constexpr int PAD = 16 / (int)sizeof(T);             // LDS row padding (elements)
     static constexpr int LDK = DK + PAD;                        // [*][DK] operand rows
     static constexpr int LDC = C + PAD;                         // [*][C] operand rows
     static constexpr int LDA = C + 4;                           // fp32 [C][C] rows
     static constexpr int KPL_DK = KplFor<T, DK>::value;
-    static constexpr int KPL_C = KplFor<T, C>::value;
     static constexpr int NPAIR = NTC * (NTC - 1) / 2;
-    static constexpr int NP = NT / DK;                          // token parts per channel
-    static constexpr int RP = C / NP;                           // tokens per part
-    static constexpr int NS_TILES = NTK * NTV, NSW = (NS_TILES + NW - 1) / NW;
-    static constexpr int NU_TILES = NTC * NTV, NUW = (NU_TILES + NW - 1) / NW;
-    static_assert(NP * DK == NT && NP * RP == C, "channel/token split");
+    // channel-pair mapping of the decay-factor phase
+    static constexpr int NPC = DK / 2;                          // channel pairs
+    static constexpr int NPART = (NT / NPC) < C ? (NT / NPC) : C;
+    static constexpr int RP = C / NPART;                        // rows per part
+    static constexpr int LPR = DK / VEC;                        // 16-byte vectors per q/k row
+    static constexpr int NQV = (C * LPR + NT - 1) / NT;
+    static_assert(NPART * RP == C && NCW <= NW && BV % 16 == 0, "shape");
 
     static constexpr size_t al(size_t x) { return (x + 15) & ~(size_t)15; }
-    static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
     static constexpr size_t szCK = al((size_t)C * LDK * sizeof(T));      // [C][DK]
     static constexpr size_t szKC = al((size_t)DK * LDC * sizeof(T));     // [DK][C]
-    static constexpr size_t szVC = al((size_t)BV * LDC * sizeof(T));     // [BV][C]
     static constexpr size_t szCC = al((size_t)C * LDA * 4);              // fp32 [C][C]
-    static constexpr size_t szS = al((size_t)BV * LDK * sizeof(T));      // [BV][DK]
     static constexpr size_t szY = al((size_t)(NTC > 1 ? NTC - 1 : 1) * 256 * 4);
     static constexpr size_t szSmall =
-        al((size_t)(2 * C + (NPAIR > 0 ? NPAIR : 1) * DK + (3 * NTC + 2 + NP) * DK) * 4);
-    static constexpr size_t oQ = 0;                    // raw q -> q*Dr (hi) -> scale q e^G
-    static constexpr size_t oK = oQ + szCK;            // raw k -> k*Dr -> k e^G
-    static constexpr size_t oE = oK + szCK;            // q*Dr lo, then (V - Kd S)^T and U^T hi/lo
-    static constexpr size_t oX = oE + mx(kSplit ? szCK : 0, NSPLIT * szVC);
-                                                       // k*Dc hi/lo, then (k e^{Gn-G})^T hi/lo
-    static constexpr size_t oV = oX + mx(NSPLIT * szCK, NSPLIT * szKC);
-    static constexpr size_t oA = oV + szVC;            // A -> T diag(beta)   (fp32)
-    static constexpr size_t oP = oA + szCC;            // scale * P           (fp32)
-    static constexpr size_t oS = oP + szCC;            // S^T operand copy
-    static constexpr size_t oY = oS + szS;
+        al((size_t)(2 * C + (NPAIR > 0 ? NPAIR : 1) * DK + (3 * NTC + 2 + NPART) * DK) * 4);
+    static constexpr size_t oQr = 0;                                // raw q
+    static constexpr size_t oKr = oQr + szCK;                       // raw k
+    static constexpr size_t oGram = oKr + szCK;                     // q*Dr, k*Dr, k*Dc (hi, lo)
+    static constexpr size_t oQd = oGram + 3 * NSPLIT * szCK;        // scale q e^G (hi, lo)
+    static constexpr size_t oKd = oQd + NSPLIT * szCK;              // k e^G (hi, lo)
+    static constexpr size_t oKrT = oKd + NSPLIT * szCK;             // (k e^{Gn-G})^T (hi, lo)
+    static constexpr size_t oA = oKrT + NSPLIT * szKC;              // A -> Tb (fp32)
+    static constexpr size_t oP = oA + szCC;                         // scale * P (fp32)
+    static constexpr size_t oY = oP + szCC;
     static constexpr size_t oSmall = oY + szY;
     static constexpr size_t kLds = oSmall + szSmall;
     static constexpr bool kFits = kLds <= 160 * 1024;
-    // load vectors per thread and chunk
-    static constexpr int LPR = DK / VEC;                        // 16-byte vectors per q/k row
-    static constexpr int NQV = (C * LPR + NT - 1) / NT;
-    static constexpr int NVV = (C * (BV / VEC) + NT - 1) / NT;
-    // Two workgroups per CU where both the LDS and the 256-register budget of a
-    // wave at that occupancy hold (wider state slices spill at two).
 #ifndef KDA_CHUNK_MIN_WG
-    static constexpr int kMinWg = (kLds <= 80 * 1024 && DK * BV <= 2048) ? 2 : 1;
+    static constexpr int kMinWg = kLds <= 80 * 1024 ? 2 : 1;
 #else
     static constexpr int kMinWg = KDA_CHUNK_MIN_WG;
 #endif
@@ -122,14 +113,15 @@ __device__ __forceinline__ int64_t chunk_seq_off(const int32_t *cu, int i, int64
     return min((int64_t)max(cu[i], 0), total);
 }
 
-__device__ __forceinline__ void scale_frag(float &f, const float *s) { f *= s[0]; }
-__device__ __forceinline__ void scale_frag(bf16x4 &f, const float *s) {
+template <class F>
+__device__ __forceinline__ void scale_frag(F &f, const float *s) {
+    if constexpr (std::is_same<F, float>::value) {
+        f *= s[0];
+    } else {
+        constexpr int n = sizeof(F) / sizeof(bf16);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) f[e] = (bf16)((float)f[e] * s[e]);
-}
-__device__ __forceinline__ void scale_frag(bf16x8 &f, const float *s) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = (bf16)((float)f[e] * s[e]);
+        for (int e = 0; e < n; ++e) f[e] = (bf16)((float)f[e] * s[e]);
+    }
 }
 
 // (hi + lo) * s re-split into a new (hi, lo) pair, in fp32.
@@ -139,71 +131,169 @@ __device__ __forceinline__ void rescale_split(F &hi, F &lo, const float *s) {
 #pragma unroll
     for (int e = 0; e < n; ++e) {
         const float x = ((float)hi[e] + (float)lo[e]) * s[e];
-        const bf16 h = (bf16)x;
-        hi[e] = h;
-        lo[e] = (bf16)(x - (float)h);
+        const bf16 hh = (bf16)x;
+        hi[e] = hh;
+        lo[e] = (bf16)(x - (float)hh);
     }
 }
 
-// A-operand fragment read from an fp32 LDS matrix [rows][ld] and split into
-// bf16 hi + lo parts (KPL consecutive k per lane, as load_frag).
-template <int KPL>
-__device__ __forceinline__ void load_frag_split(const float *M, int ld, int row0, int k0, int lane,
-                                                typename Frag<bf16, KPL>::type &hi,
-                                                typename Frag<bf16, KPL>::type &lo) {
-    const float *p = M + (row0 + (lane & 15)) * ld + k0 + (lane >> 4) * KPL;
+__device__ __forceinline__ void split2(float x, bf16 &hh, bf16 &ll) {
+    hh = (bf16)x;
+    ll = (bf16)(x - (float)hh);
+}
+
+// ---------------------------------------------------------------------------
+// Products whose B operand is an accumulator tile held in registers.
+//
+// An accumulator tile holds B[(l >> 4) * 4 + r][l & 15] in element r of lane l.
+// For a 32-row k block made of two such tiles (a: rows 0-15, b: rows 16-31), the
+// lane's 8 B values are rows {(l>>4)*4 + 0..3} of a and of b; the hardware pairs
+// A and B entries by (lane group, element), so the A fragment is read with the
+// same k order: A[row][k0 + (l>>4)*4 + 0..3] and A[row][k0 + 16 + (l>>4)*4 + 0..3].
+// A 16-row block uses the 16x16x16 instruction with one tile.  fp32 uses four
+// 16x16x4 steps per 16-row block, step s taking element s.
+// ---------------------------------------------------------------------------
+struct BReg8 { bf16x8 h, l; };
+struct BReg4 { bf16x4 h, l; };
+
+__device__ __forceinline__ BReg8 breg8(const f32x4 &a, const f32x4 &b) {
+    BReg8 r;
 #pragma unroll
-    for (int e = 0; e < KPL; ++e) {
-        const float x = p[e];
-        const bf16 h = (bf16)x;
-        hi[e] = h;
-        lo[e] = (bf16)(x - (float)h);
+    for (int e = 0; e < 4; ++e) {
+        bf16 hh, ll;
+        split2(a[e], hh, ll); r.h[e] = hh; r.l[e] = ll;
+        split2(b[e], hh, ll); r.h[e + 4] = hh; r.l[e + 4] = ll;
+    }
+    return r;
+}
+__device__ __forceinline__ BReg4 breg4(const f32x4 &a) {
+    BReg4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf16 hh, ll;
+        split2(a[e], hh, ll); r.h[e] = hh; r.l[e] = ll;
+    }
+    return r;
+}
+
+// A fragments (hi, lo) from bf16 LDS matrices [rows][ld], permuted k order.
+__device__ __forceinline__ void afrag8(const bf16 *Mh, const bf16 *Ml, int ld, int row0, int k0,
+                                       int lane, bf16x8 &hh, bf16x8 &ll) {
+    const int off = (row0 + (lane & 15)) * ld + k0 + (lane >> 4) * 4;
+    const bf16x4 h0 = *reinterpret_cast<const bf16x4 *>(Mh + off);
+    const bf16x4 h1 = *reinterpret_cast<const bf16x4 *>(Mh + off + 16);
+    const bf16x4 l0 = *reinterpret_cast<const bf16x4 *>(Ml + off);
+    const bf16x4 l1 = *reinterpret_cast<const bf16x4 *>(Ml + off + 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        hh[e] = h0[e]; hh[e + 4] = h1[e];
+        ll[e] = l0[e]; ll[e + 4] = l1[e];
+    }
+}
+__device__ __forceinline__ void afrag4(const bf16 *Mh, const bf16 *Ml, int ld, int row0, int k0,
+                                       int lane, bf16x4 &hh, bf16x4 &ll) {
+    const int off = (row0 + (lane & 15)) * ld + k0 + (lane >> 4) * 4;
+    hh = *reinterpret_cast<const bf16x4 *>(Mh + off);
+    ll = *reinterpret_cast<const bf16x4 *>(Ml + off);
+}
+// ... from an fp32 LDS matrix, split on the fly.
+__device__ __forceinline__ void afrag8_f32(const float *M, int ld, int row0, int k0, int lane,
+                                           bf16x8 &hh, bf16x8 &ll) {
+    const float *p = M + (row0 + (lane & 15)) * ld + k0 + (lane >> 4) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf16 a, c;
+        split2(p[e], a, c); hh[e] = a; ll[e] = c;
+        split2(p[e + 16], a, c); hh[e + 4] = a; ll[e + 4] = c;
+    }
+}
+__device__ __forceinline__ void afrag4_f32(const float *M, int ld, int row0, int k0, int lane,
+                                           bf16x4 &hh, bf16x4 &ll) {
+    const float *p = M + (row0 + (lane & 15)) * ld + k0 + (lane >> 4) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf16 a, c;
+        split2(p[e], a, c); hh[e] = a; ll[e] = c;
     }
 }
 
-// D += A B^T-style tile product where A comes from an fp32 LDS matrix and B from
-// k-contiguous hi (and lo) operand matrices in T.  With T = bf16 the product is
-// the three-term split product; with T = fp32 it is a plain fp32 product.
-template <class T, int KPL>
-__device__ __forceinline__ f32x4 tile_mma_f32a(f32x4 acc, const float *A, int lda, int arow0,
-                                               const T *Bh, const T *Bl, int ldb, int brow0,
-                                               int kend, int lane) {
-    for (int k0 = 0; k0 < kend; k0 += 4 * KPL) {
+__device__ __forceinline__ f32x4 mma3(const bf16x8 &ah, const bf16x8 &al, const BReg8 &bb,
+                                      f32x4 c) {
+    c = mma(ah, bb.h, c);
+    c = mma(ah, bb.l, c);
+    return mma(al, bb.h, c);
+}
+__device__ __forceinline__ f32x4 mma3(const bf16x4 &ah, const bf16x4 &al, const BReg4 &bb,
+                                      f32x4 c) {
+    c = mma(ah, bb.h, c);
+    c = mma(ah, bb.l, c);
+    return mma(al, bb.h, c);
+}
+
+// D += A[row0.., 0..16*nb) * B, with B given as NBLK 16-row accumulator tiles
+// (prepared once, used for several products).  A comes from (hi, lo) matrices in
+// T (Mh, Ml) or from an fp32 matrix (Mf).  bf16: three-term split products;
+// fp32: plain fp32 MFMA.
+template <class T, int NBLK>
+struct RegB {
+    BReg8 b8[NBLK / 2 > 0 ? NBLK / 2 : 1];
+    BReg4 b4;
+    const f32x4 *tiles;
+    __device__ __forceinline__ void prepare(const f32x4 *t) {
+        tiles = t;
         if constexpr (std::is_same<T, bf16>::value) {
-            typename Frag<bf16, KPL>::type ah, al;
-            load_frag_split<KPL>(A, lda, arow0, k0, lane, ah, al);
-            auto bh = load_frag<T, KPL>(Bh, ldb, brow0, k0, lane);
-            auto bl = load_frag<T, KPL>(Bl, ldb, brow0, k0, lane);
-            acc = mma(ah, bh, acc);
-            acc = mma(ah, bl, acc);
-            acc = mma(al, bh, acc);
+#pragma unroll
+            for (int j = 0; j < NBLK / 2; ++j) b8[j] = breg8(t[2 * j], t[2 * j + 1]);
+            if constexpr (NBLK % 2) b4 = breg4(t[NBLK - 1]);
+        }
+    }
+    __device__ __forceinline__ f32x4 mul(f32x4 acc, const T *Mh, const T *Ml, const float *Mf,
+                                         int ld, int row0, int nb, int lane) const {
+        if constexpr (std::is_same<T, bf16>::value) {
+#pragma unroll
+            for (int j = 0; j < NBLK / 2; ++j) {
+                if (2 * j < nb) {
+                    if (2 * j + 1 < nb) {
+                        bf16x8 ah, al;
+                        if (Mf) afrag8_f32(Mf, ld, row0, 32 * j, lane, ah, al);
+                        else afrag8(Mh, Ml, ld, row0, 32 * j, lane, ah, al);
+                        acc = mma3(ah, al, b8[j], acc);
+                    } else {   // only the first tile of this pair is inside the range
+                        bf16x4 ah, al;
+                        if (Mf) afrag4_f32(Mf, ld, row0, 32 * j, lane, ah, al);
+                        else afrag4(Mh, Ml, ld, row0, 32 * j, lane, ah, al);
+                        BReg4 bb;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { bb.h[e] = b8[j].h[e]; bb.l[e] = b8[j].l[e]; }
+                        acc = mma3(ah, al, bb, acc);
+                    }
+                }
+            }
+            if constexpr (NBLK % 2) {
+                if (NBLK - 1 < nb) {
+                    bf16x4 ah, al;
+                    if (Mf) afrag4_f32(Mf, ld, row0, 16 * (NBLK - 1), lane, ah, al);
+                    else afrag4(Mh, Ml, ld, row0, 16 * (NBLK - 1), lane, ah, al);
+                    acc = mma3(ah, al, b4, acc);
+                }
+            }
         } else {
-            const float a = A[(arow0 + (lane & 15)) * lda + k0 + (lane >> 4)];
-            auto b = load_frag<T, KPL>(Bh, ldb, brow0, k0, lane);
-            acc = mma(a, b, acc);
+#pragma unroll
+            for (int j = 0; j < NBLK; ++j) {
+                if (j < nb) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int col = 16 * j + (lane >> 4) * 4 + s;
+                        const float a = Mf ? Mf[(row0 + (lane & 15)) * ld + col]
+                                           : (float)Mh[(row0 + (lane & 15)) * ld + col];
+                        acc = mma(a, tiles[j][s], acc);
+                    }
+                }
+            }
         }
+        return acc;
     }
-    return acc;
-}
-
-// Same with both operands as (hi, lo) pairs in T (three-term product for bf16).
-template <class T, int KPL>
-__device__ __forceinline__ f32x4 tile_mma_split(f32x4 acc, const T *Ah, const T *Al, int lda,
-                                                int arow0, const T *Bh, const T *Bl, int ldb,
-                                                int brow0, int kend, int lane) {
-    for (int k0 = 0; k0 < kend; k0 += 4 * KPL) {
-        auto ah = load_frag<T, KPL>(Ah, lda, arow0, k0, lane);
-        auto bh = load_frag<T, KPL>(Bh, ldb, brow0, k0, lane);
-        acc = mma(ah, bh, acc);
-        if constexpr (std::is_same<T, bf16>::value) {
-            auto al = load_frag<T, KPL>(Al, lda, arow0, k0, lane);
-            auto bl = load_frag<T, KPL>(Bl, ldb, brow0, k0, lane);
-            acc = mma(ah, bl, acc);
-            acc = mma(al, bh, acc);
-        }
-    }
-    return acc;
-}
+};
 
 template <class T, class TO, int DK, int BV, int C>
 __global__ __launch_bounds__(256, (ChunkCfg<T, DK, BV, C>::kMinWg))
@@ -214,26 +304,30 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
                   TO *__restrict__ o, int units, int nslice) {
     using Cfg = ChunkCfg<T, DK, BV, C>;
     constexpr bool SPLIT = Cfg::kSplit;
-    constexpr int NW = Cfg::NW, NT = Cfg::NT, NTC = Cfg::NTC, NTK = Cfg::NTK, NTV = Cfg::NTV;
+    constexpr int NW = Cfg::NW, NT = Cfg::NT, NTC = Cfg::NTC, NTK = Cfg::NTK, NCW = Cfg::NCW;
     constexpr int VEC = Cfg::VEC, LDK = Cfg::LDK, LDC = Cfg::LDC, LDA = Cfg::LDA;
-    constexpr int KPL_DK = Cfg::KPL_DK, KPL_C = Cfg::KPL_C, KSTEP_C = 4 * KPL_C;
-    constexpr int RP = Cfg::RP;
+    constexpr int KPL_DK = Cfg::KPL_DK, NPC = Cfg::NPC, NPART = Cfg::NPART, RP = Cfg::RP;
+    constexpr int LPR = Cfg::LPR, NQV = Cfg::NQV;
     typedef typename Vec16<T>::type VT;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::kLds];
-    T *sQ = reinterpret_cast<T *>(smem + Cfg::oQ);                    // q*Dr hi
-    T *sQL = reinterpret_cast<T *>(smem + Cfg::oE);                   // q*Dr lo
-    T *sK = reinterpret_cast<T *>(smem + Cfg::oK);
-    T *sX = reinterpret_cast<T *>(smem + Cfg::oX);                    // k*Dc hi (Gram columns)
-    T *sXL = reinterpret_cast<T *>(smem + Cfg::oX + (SPLIT ? Cfg::szCK : 0));  // k*Dc lo
-    T *sKrH = reinterpret_cast<T *>(smem + Cfg::oX);                  // (k e^{Gn-G})^T hi
-    T *sKrL = reinterpret_cast<T *>(smem + Cfg::oX + (SPLIT ? Cfg::szKC : 0));
-    T *sVT = reinterpret_cast<T *>(smem + Cfg::oV);                   // V^T slice
-    float *sA = reinterpret_cast<float *>(smem + Cfg::oA);            // A -> Tb
-    float *sPf = reinterpret_cast<float *>(smem + Cfg::oP);           // scale * P
-    T *sEH = reinterpret_cast<T *>(smem + Cfg::oE);                   // E^T / U^T hi
-    T *sEL = reinterpret_cast<T *>(smem + Cfg::oE + (SPLIT ? Cfg::szVC : 0));
-    T *sST = reinterpret_cast<T *>(smem + Cfg::oS);                   // S^T operand
+    T *sQr = reinterpret_cast<T *>(smem + Cfg::oQr);
+    T *sKr = reinterpret_cast<T *>(smem + Cfg::oKr);
+    constexpr size_t CKE = Cfg::szCK / sizeof(T), KCE = Cfg::szKC / sizeof(T);
+    T *sQDh = reinterpret_cast<T *>(smem + Cfg::oGram);
+    T *sKDh = sQDh + Cfg::NSPLIT * CKE;
+    T *sKCh = sKDh + Cfg::NSPLIT * CKE;
+    T *sQDl = sQDh + (SPLIT ? CKE : 0);
+    T *sKDl = sKDh + (SPLIT ? CKE : 0);
+    T *sKCl = sKCh + (SPLIT ? CKE : 0);
+    T *sQdh = reinterpret_cast<T *>(smem + Cfg::oQd);
+    T *sQdl = sQdh + (SPLIT ? CKE : 0);
+    T *sKdh = reinterpret_cast<T *>(smem + Cfg::oKd);
+    T *sKdl = sKdh + (SPLIT ? CKE : 0);
+    T *sKrTh = reinterpret_cast<T *>(smem + Cfg::oKrT);
+    T *sKrTl = sKrTh + (SPLIT ? KCE : 0);
+    float *sA = reinterpret_cast<float *>(smem + Cfg::oA);
+    float *sPf = reinterpret_cast<float *>(smem + Cfg::oP);
     float *sY = reinterpret_cast<float *>(smem + Cfg::oY);
     float *sBeta = reinterpret_cast<float *>(smem + Cfg::oSmall);
     float *sPd = sBeta + C;                                            // scale q_t . k_t
@@ -259,43 +353,30 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
     const int64_t eos = max(chunk_seq_off(cu_seqlens, n + 1, total), bos);
     const int v0 = slice * BV;
     const size_t rowQK = (size_t)H * DK, rowV = (size_t)H * DV;
+    const bool owner = wave < NCW;                           // this wave owns state columns
+    const int vc = v0 + (owner ? wave : 0) * 16 + (lane & 15);  // its value column
 
-    // ---- state slice: accumulator tiles (rt, ct), tile id = rt*NTV + ct, wave = id % NW
-    f32x4 Sacc[Cfg::NSW];
+    // ---- state: tiles rt = 0..NTK-1 of rows [16 rt, 16 rt + 16), columns of this wave
+    f32x4 Sacc[NTK];
 #pragma unroll
-    for (int i = 0; i < Cfg::NSW; ++i) {
-        const int id = wave + i * NW;
-        Sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (id < Cfg::NS_TILES && h0) {
-            const int rt = id / NTV, ct = id % NTV;
-            const float *src = h0 + ((size_t)unit * DK) * DV + v0;
+    for (int rt = 0; rt < NTK; ++rt) {
+        Sacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (owner && h0) {
+            const float *src = h0 + ((size_t)unit * DK) * DV;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                Sacc[i][r] = src[(size_t)(rt * 16 + acc_row(lane, r)) * DV + ct * 16 + acc_col(lane)];
+                Sacc[rt][r] = src[(size_t)(rt * 16 + acc_row(lane, r)) * DV + vc];
         }
     }
-    auto store_state_operand = [&]() {
-#pragma unroll
-        for (int i = 0; i < Cfg::NSW; ++i) {
-            const int id = wave + i * NW;
-            if (id < Cfg::NS_TILES) {
-                const int rt = id / NTV, ct = id % NTV;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sST[(ct * 16 + acc_col(lane)) * LDK + rt * 16 + acc_row(lane, r)] =
-                        from_f32<T>(Sacc[i][r]);
-            }
-        }
-    };
-    store_state_operand();
 
-    // channel-owner mapping used for the decay factors: channel c, tokens [part*RP, +RP)
-    const int cc = tid % DK, part = tid / DK;
-    constexpr int LPR = Cfg::LPR, NQV = Cfg::NQV, NVV = Cfg::NVV, VPR = BV / VEC;
+    // channel-pair mapping of the decay-factor phase: channels 2cp, 2cp+1, rows [part*RP, +RP)
+    const int cp = tid % NPC, part = tid / NPC;
+    const bool fthread = part < NPART;
 
     // ---- registers holding the next chunk's inputs (rows clamped into the sequence)
-    VT pq[NQV], pk[NQV], pv[NVV];
-    float pg[RP], pb = 0.f;
+    VT pq[NQV], pk[NQV];
+    float pv[NTC][4];
+    float pg[RP][2], pb = 0.f;
     auto issue_loads = [&](int64_t cs) {
         const int last = (int)min((int64_t)C, eos - cs) - 1;
 #pragma unroll
@@ -308,18 +389,24 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
                 pk[j] = *reinterpret_cast<const VT *>(k + off);
             }
         }
+        if (owner) {
 #pragma unroll
-        for (int j = 0; j < NVV; ++j) {
-            const int idx = tid + j * NT;
-            if (C * VPR % NT == 0 || idx < C * VPR) {
-                const int r = min(idx / VPR, last), cv = idx % VPR;
-                pv[j] = *reinterpret_cast<const VT *>(v + (size_t)(cs + r) * rowV + (size_t)h * DV +
-                                                      v0 + cv * VEC);
+            for (int R = 0; R < NTC; ++R)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = min(R * 16 + acc_row(lane, r), last);
+                    pv[R][r] = to_f32(v[(size_t)(cs + t) * rowV + (size_t)h * DV + vc]);
+                }
+        }
+        if (fthread) {
+#pragma unroll
+            for (int j = 0; j < RP; ++j) {
+                const float2 gg = *reinterpret_cast<const float2 *>(
+                    g + (size_t)(cs + min(part * RP + j, last)) * rowQK + (size_t)h * DK + 2 * cp);
+                pg[j][0] = gg.x;
+                pg[j][1] = gg.y;
             }
         }
-#pragma unroll
-        for (int j = 0; j < RP; ++j)
-            pg[j] = g[(size_t)(cs + min(part * RP + j, last)) * rowQK + (size_t)h * DK + cc];
         if (tid < C) pb = beta[(size_t)(cs + min(tid, last)) * H + h];
     };
     if (bos < eos) issue_loads(bos);
@@ -335,9 +422,9 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
                 const int r = idx / LPR, cv = idx % LPR;
                 const VT qv = r < nt ? pq[j] : VT{};
                 const VT kv = r < nt ? pk[j] : VT{};
-                *reinterpret_cast<VT *>(sQ + r * LDK + cv * VEC) = qv;
-                *reinterpret_cast<VT *>(sK + r * LDK + cv * VEC) = kv;
-                // exact diagonal of P: scale * q_r . k_r (products of bf16 are exact in fp32)
+                *reinterpret_cast<VT *>(sQr + r * LDK + cv * VEC) = qv;
+                *reinterpret_cast<VT *>(sKr + r * LDK + cv * VEC) = kv;
+                // exact diagonal of P: scale * q_r . k_r
                 float dot = 0.f;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) dot += to_f32(qv[e]) * to_f32(kv[e]);
@@ -345,80 +432,114 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
                 if (cv == 0) sPd[r] = scale * dot;
             }
         }
-#pragma unroll
-        for (int j = 0; j < NVV; ++j) {
-            const int idx = tid + j * NT;
-            if (C * VPR % NT == 0 || idx < C * VPR) {
-                const int r = idx / VPR, cv = idx % VPR;
-                const VT vv = r < nt ? pv[j] : VT{};
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) sVT[(cv * VEC + e) * LDC + r] = vv[e];
-            }
-        }
         if (tid < C) sBeta[tid] = tid < nt ? pb : 0.f;
+        float vin[NTC][4];
+#pragma unroll
+        for (int R = 0; R < NTC; ++R)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) vin[R][r] = (R * 16 + acc_row(lane, r) < nt) ? pv[R][r] : 0.f;
 
-        // cumulative log2-decay of channel cc over this thread's tokens (registers)
-        float gam[RP];
-        {
-            float acc = 0.f;
+        // cumulative log2-decay of channels 2cp, 2cp+1 over this thread's rows
+        float gam[RP][2];
+        if (fthread) {
+            float a0 = 0.f, a1 = 0.f;
 #pragma unroll
             for (int j = 0; j < RP; ++j) {
-                acc += (part * RP + j < nt ? pg[j] : 0.f) * kLog2e;
-                gam[j] = acc;
+                const bool in = part * RP + j < nt;
+                a0 += (in ? pg[j][0] : 0.f) * kLog2e;
+                a1 += (in ? pg[j][1] : 0.f) * kLog2e;
+                gam[j][0] = a0;
+                gam[j][1] = a1;
             }
-            sTot[part * DK + cc] = acc;
+            sTot[part * DK + 2 * cp] = a0;
+            sTot[part * DK + 2 * cp + 1] = a1;
         }
         // the next chunk's loads fly while this chunk is computed
         if (c0 + C < eos) issue_loads(c0 + C);
         __syncthreads();
-        {
-            float off = 0.f;
-            for (int p = 0; p < part; ++p) off += sTot[p * DK + cc];
+        if (fthread) {
+            float o0 = 0.f, o1 = 0.f;
+            for (int p = 0; p < part; ++p) {
+                o0 += sTot[p * DK + 2 * cp];
+                o1 += sTot[p * DK + 2 * cp + 1];
+            }
 #pragma unroll
             for (int j = 0; j < RP; ++j) {
-                gam[j] += off;
+                gam[j][0] += o0;
+                gam[j][1] += o1;
                 const int r = part * RP + j;
-                if ((r & 15) == 8) sGm[(r >> 4) * DK + cc] = gam[j];
-                if ((r & 15) == 0) sGs[(r >> 4) * DK + cc] = gam[j];
-                if (r == C - 1) sGl[cc] = gam[j];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int c = 2 * cp + e;
+                    if ((r & 15) == 8) sGm[(r >> 4) * DK + c] = gam[j][e];
+                    if ((r & 15) == 0) sGs[(r >> 4) * DK + c] = gam[j][e];
+                    if (r == C - 1) sGl[c] = gam[j][e];
+                }
             }
         }
         __syncthreads();
 
         // ================= F: decay factors =================
-        // Gram operands to LDS: q e^{G_t-G_m} (hi, lo), k e^{G_t-G_m}, k e^{G_m-G_t} (hi, lo)
-        // (m = middle row of t's 16-token tile).  Raw q, k stay in registers for the
-        // chunk-level operands, formed after the Gram products.
-        T rq[RP], rk[RP];
-        {
+        // Gram operands (hi, lo): q e^{G_t-G_m}, k e^{G_t-G_m}, k e^{G_m-G_t} (m = middle row
+        // of t's 16-token tile).  Chunk operands (hi, lo): scale q e^{G_t}, k e^{G_t},
+        // (k e^{G_n-G_t})^T.
+        if (fthread) {
+            float qv[RP][2], kv[RP][2];
 #pragma unroll
             for (int j = 0; j < RP; ++j) {
                 const int r = part * RP + j;
-                const float d = gam[j] - sGm[(r >> 4) * DK + cc];
-                const float dr = exp2_clamped(d), dc = exp2_clamped(-d);
-                rq[j] = sQ[r * LDK + cc];
-                rk[j] = sK[r * LDK + cc];
-                const float qf = to_f32(rq[j]), kf = to_f32(rk[j]);
-                const float qd = qf * dr, kc = kf * dc;
-                const T qdh = from_f32<T>(qd), kch = from_f32<T>(kc);
-                sQ[r * LDK + cc] = qdh;
-                sK[r * LDK + cc] = from_f32<T>(kf * dr);
-                sX[r * LDK + cc] = kch;
-                if constexpr (SPLIT) {
-                    sQL[r * LDK + cc] = from_f32<T>(qd - to_f32(qdh));
-                    sXL[r * LDK + cc] = from_f32<T>(kc - to_f32(kch));
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    qv[j][e] = to_f32(sQr[r * LDK + 2 * cp + e]);
+                    kv[j][e] = to_f32(sKr[r * LDK + 2 * cp + e]);
                 }
             }
-            if (part == 0) {
-                sEGn[cc] = exp2_clamped(sGl[cc]);
+            float krt[2][RP];
 #pragma unroll
-                for (int R = 1; R < NTC; ++R) {
-                    sRsc[R * DK + cc] = exp2_clamped(sGm[R * DK + cc] - sGs[R * DK + cc]);
+            for (int j = 0; j < RP; ++j) {
+                const int r = part * RP + j;
 #pragma unroll
-                    for (int I = 0; I < R; ++I)
-                        sBnd[(R * (R - 1) / 2 + I) * DK + cc] =
-                            exp2_clamped(sGs[R * DK + cc] - sGm[I * DK + cc]);
+                for (int e = 0; e < 2; ++e) {
+                    const int c = 2 * cp + e;
+                    const float gt = gam[j][e];
+                    const float d = gt - sGm[(r >> 4) * DK + c];
+                    const float dr = exp2_clamped(d), dc = exp2_clamped(-d);
+                    const float eg = exp2_clamped(gt), egr = exp2_clamped(sGl[c] - gt);
+                    const float qf = qv[j][e], kf = kv[j][e];
+                    const int i = r * LDK + c;
+                    auto put = [&](T *Hh, T *Ll, float x) {
+                        const T hh = from_f32<T>(x);
+                        Hh[i] = hh;
+                        if constexpr (SPLIT) Ll[i] = from_f32<T>(x - to_f32(hh));
+                    };
+                    put(sQDh, sQDl, qf * dr);
+                    put(sKDh, sKDl, kf * dr);
+                    put(sKCh, sKCl, kf * dc);
+                    put(sQdh, sQdl, qf * eg * scale);
+                    put(sKdh, sKdl, kf * eg);
+                    krt[e][j] = kf * egr;
                 }
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int j = 0; j < RP; ++j) {
+                    const int i = (2 * cp + e) * LDC + part * RP + j;
+                    const T kh = from_f32<T>(krt[e][j]);
+                    sKrTh[i] = kh;
+                    if constexpr (SPLIT) sKrTl[i] = from_f32<T>(krt[e][j] - to_f32(kh));
+                }
+        }
+        if (tid < DK) {
+            const int c = tid;
+            sEGn[c] = exp2_clamped(sGl[c]);
+#pragma unroll
+            for (int R = 1; R < NTC; ++R) {
+                sRsc[R * DK + c] = exp2_clamped(sGm[R * DK + c] - sGs[R * DK + c]);
+#pragma unroll
+                for (int I = 0; I < R; ++I)
+                    sBnd[(R * (R - 1) / 2 + I) * DK + c] =
+                        exp2_clamped(sGs[R * DK + c] - sGm[I * DK + c]);
             }
         }
         __syncthreads();
@@ -431,29 +552,32 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
                 const float *bnd = sBnd + (I < R ? (R * (R - 1) / 2 + I) * DK : 0);
                 const float *rsc = sRsc + R * DK;
                 for (int k0 = 0; k0 < DK; k0 += 4 * KPL_DK) {
-                    auto ak = load_frag<T, KPL_DK>(sK, LDK, R * 16, k0, lane);
-                    auto qh = load_frag<T, KPL_DK>(sQ, LDK, R * 16, k0, lane);
-                    auto ch = load_frag<T, KPL_DK>(sX, LDK, I * 16, k0, lane);
+                    auto kh = load_frag<T, KPL_DK>(sKDh, LDK, R * 16, k0, lane);
+                    auto qh = load_frag<T, KPL_DK>(sQDh, LDK, R * 16, k0, lane);
+                    auto ch = load_frag<T, KPL_DK>(sKCh, LDK, I * 16, k0, lane);
                     if constexpr (SPLIT) {
-                        auto ql = load_frag<T, KPL_DK>(sQL, LDK, R * 16, k0, lane);
-                        auto cl = load_frag<T, KPL_DK>(sXL, LDK, I * 16, k0, lane);
+                        auto kl = load_frag<T, KPL_DK>(sKDl, LDK, R * 16, k0, lane);
+                        auto ql = load_frag<T, KPL_DK>(sQDl, LDK, R * 16, k0, lane);
+                        auto cl = load_frag<T, KPL_DK>(sKCl, LDK, I * 16, k0, lane);
                         if (I < R) {   // re-reference rows and columns to s_R
                             const int kk = k0 + (lane >> 4) * KPL_DK;
-                            scale_frag(ak, rsc + kk);
+                            rescale_split(kh, kl, rsc + kk);
                             rescale_split(qh, ql, rsc + kk);
                             rescale_split(ch, cl, bnd + kk);
                         }
+                        accA = mma(kh, cl, accA);
+                        accA = mma(kl, ch, accA);
                         accP = mma(qh, cl, accP);
                         accP = mma(ql, ch, accP);
                     } else {
                         if (I < R) {
                             const int kk = k0 + (lane >> 4) * KPL_DK;
-                            scale_frag(ak, rsc + kk);
+                            scale_frag(kh, rsc + kk);
                             scale_frag(qh, rsc + kk);
                             scale_frag(ch, bnd + kk);
                         }
                     }
-                    accA = mma(ak, ch, accA);
+                    accA = mma(kh, ch, accA);
                     accP = mma(qh, ch, accP);
                 }
             }
@@ -466,24 +590,8 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
         }
         __syncthreads();
 
-        // ================= X: chunk-level operands; inverse diagonal blocks =================
-        // scale q e^{G_t} over q*Dr, k e^{G_t} over k*Dr, (k e^{G_n-G_t})^T hi/lo over k*Dc
-        {
-            const float gl = sGl[cc];
-#pragma unroll
-            for (int j = 0; j < RP; ++j) {
-                const int r = part * RP + j;
-                const float eg = exp2_clamped(gam[j]), egr = exp2_clamped(gl - gam[j]);
-                const float qf = to_f32(rq[j]), kf = to_f32(rk[j]);
-                sQ[r * LDK + cc] = from_f32<T>(qf * eg * scale);
-                sK[r * LDK + cc] = from_f32<T>(kf * eg);
-                const float kr = kf * egr;
-                const T krh = from_f32<T>(kr);
-                sKrH[cc * LDC + r] = krh;
-                if constexpr (SPLIT) sKrL[cc * LDC + r] = from_f32<T>(kr - to_f32(krh));
-            }
-        }
-        // diagonal 16x16 blocks of (I + diag(beta) A)^{-1}: lane i builds column i
+        // ================= I: Tb = (I + diag(beta) A)^{-1} diag(beta) =================
+        // diagonal 16x16 blocks: lane i builds column i by forward substitution
         for (int R = wave; R < NTC; R += NW) {
             const int i = lane;
             float x[16];
@@ -492,8 +600,8 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
                 const float br = sBeta[R * 16 + r];
                 float s = 0.f;
 #pragma unroll
-                for (int m2 = 0; m2 < r; ++m2) s += br * sA[(R * 16 + r) * LDA + R * 16 + m2] * x[m2];
-                x[r] = (r == i) ? 1.f : (r < i ? 0.f : -s);
+                for (int m2 = 0; m2 < r; ++m2) s += sA[(R * 16 + r) * LDA + R * 16 + m2] * x[m2];
+                x[r] = (r == i) ? 1.f : (r < i ? 0.f : -br * s);
             }
             if (i < 16) {
 #pragma unroll
@@ -501,7 +609,6 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
             }
         }
         __syncthreads();
-
         // off-diagonal blocks, one block row at a time (fp32 MFMA)
         for (int R = 1; R < NTC; ++R) {
             // Y_I = sum_{M=I}^{R-1} diag(beta_R) A_RM X_MI
@@ -536,105 +643,63 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
             const int r = idx / C, i = idx % C;
             sA[r * LDA + i] *= sBeta[i];
         }
-
-        // ================= E = V - Kd S -> E^T (hi, lo);  O = Qd S =================
-        f32x4 Uacc[Cfg::NUW], Oacc[Cfg::NUW];
-#pragma unroll
-        for (int i = 0; i < Cfg::NUW; ++i) {
-            const int id = wave + i * NW;
-            Uacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            Oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (id < Cfg::NU_TILES) {
-                const int R = id / NTV, cv = id % NTV;
-                f32x4 ks = tile_mma<T, KPL_DK>(f32x4{0.f, 0.f, 0.f, 0.f}, sK, LDK, R * 16, sST,
-                                               LDK, cv * 16, 0, DK, lane);
-                Oacc[i] = tile_mma<T, KPL_DK>(Oacc[i], sQ, LDK, R * 16, sST, LDK, cv * 16, 0, DK,
-                                              lane);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = R * 16 + acc_row(lane, r), vc = cv * 16 + acc_col(lane);
-                    const float e = to_f32(sVT[vc * LDC + t]) - ks[r];
-                    const T eh = from_f32<T>(e);
-                    sEH[vc * LDC + t] = eh;
-                    if constexpr (SPLIT) sEL[vc * LDC + t] = from_f32<T>(e - to_f32(eh));
-                }
-            }
-        }
         __syncthreads();
 
-        // ================= U = Tb E  (three-term split product) =================
+        // ============ chain (state-column owners, registers only, no barriers) ============
+        if (owner) {
+            RegB<T, NTK> Sb;
+            Sb.prepare(Sacc);
+            f32x4 Et[NTC], Ot[NTC], Ut[NTC];
 #pragma unroll
-        for (int i = 0; i < Cfg::NUW; ++i) {
-            const int id = wave + i * NW;
-            if (id < Cfg::NU_TILES) {
-                const int R = id / NTV, cv = id % NTV;
-                const int kend = min(((R + 1) * 16 + KSTEP_C - 1) / KSTEP_C * KSTEP_C, C);
-                Uacc[i] = tile_mma_f32a<T, KPL_C>(Uacc[i], sA, LDA, R * 16, sEH, sEL, LDC, cv * 16,
-                                                  kend, lane);
+            for (int R = 0; R < NTC; ++R) {
+                // E = V - Kd S
+                const f32x4 ks = Sb.mul(f32x4{0.f, 0.f, 0.f, 0.f}, sKdh, sKdl, nullptr, LDK,
+                                        R * 16, NTK, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Et[R][r] = vin[R][r] - ks[r];
+                // O = Qd S
+                Ot[R] = Sb.mul(f32x4{0.f, 0.f, 0.f, 0.f}, sQdh, sQdl, nullptr, LDK, R * 16, NTK,
+                               lane);
             }
-        }
-        __syncthreads();   // every wave has consumed E before U^T overwrites it
+            // U = Tb E
+            RegB<T, NTC> Eb;
+            Eb.prepare(Et);
 #pragma unroll
-        for (int i = 0; i < Cfg::NUW; ++i) {
-            const int id = wave + i * NW;
-            if (id < Cfg::NU_TILES) {
-                const int R = id / NTV, cv = id % NTV;
+            for (int R = 0; R < NTC; ++R)
+                Ut[R] = Eb.mul(f32x4{0.f, 0.f, 0.f, 0.f}, nullptr, nullptr, sA, LDA, R * 16, R + 1,
+                               lane);
+            // O += P U
+            RegB<T, NTC> Ub;
+            Ub.prepare(Ut);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = R * 16 + acc_row(lane, r), vc = cv * 16 + acc_col(lane);
-                    const T uh = from_f32<T>(Uacc[i][r]);
-                    sEH[vc * LDC + t] = uh;
-                    if constexpr (SPLIT) sEL[vc * LDC + t] = from_f32<T>(Uacc[i][r] - to_f32(uh));
-                }
-            }
-        }
-        __syncthreads();
-
-        // ============ O += P U -> global ;  S = e^{Gn} S + (K e^{Gn-G})^T U ============
-#pragma unroll
-        for (int i = 0; i < Cfg::NUW; ++i) {
-            const int id = wave + i * NW;
-            if (id < Cfg::NU_TILES) {
-                const int R = id / NTV, cv = id % NTV;
-                const int kend = min(((R + 1) * 16 + KSTEP_C - 1) / KSTEP_C * KSTEP_C, C);
-                Oacc[i] = tile_mma_f32a<T, KPL_C>(Oacc[i], sPf, LDA, R * 16, sEH, sEL, LDC, cv * 16,
-                                                  kend, lane);
+            for (int R = 0; R < NTC; ++R) {
+                Ot[R] = Ub.mul(Ot[R], nullptr, nullptr, sPf, LDA, R * 16, R + 1, lane);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = R * 16 + acc_row(lane, r);
                     if (row < nt)
-                        o[(size_t)(c0 + row) * rowV + (size_t)h * DV + v0 + cv * 16 + acc_col(lane)] =
-                            from_f32<TO>(Oacc[i][r]);
+                        o[(size_t)(c0 + row) * rowV + (size_t)h * DV + vc] = from_f32<TO>(Ot[R][r]);
                 }
             }
-        }
+            // S = diag(e^{G_n}) S + Kr^T U
 #pragma unroll
-        for (int i = 0; i < Cfg::NSW; ++i) {
-            const int id = wave + i * NW;
-            if (id < Cfg::NS_TILES) {
-                const int rt = id / NTV, ct = id % NTV;
+            for (int rt = 0; rt < NTK; ++rt) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Sacc[i][r] *= sEGn[rt * 16 + acc_row(lane, r)];
-                Sacc[i] = tile_mma_split<T, KPL_C>(Sacc[i], sKrH, sKrL, LDC, rt * 16, sEH, sEL, LDC,
-                                                   ct * 16, C, lane);
+                for (int r = 0; r < 4; ++r) Sacc[rt][r] *= sEGn[rt * 16 + acc_row(lane, r)];
+                Sacc[rt] = Ub.mul(Sacc[rt], sKrTh, sKrTl, nullptr, LDC, rt * 16, NTC, lane);
             }
         }
-        store_state_operand();
-        __syncthreads();
+        // No barrier here: the next chunk's first barrier orders every read above
+        // before the LDS writes that follow it.
     }
 
-    if (hT) {
+    if (hT && owner) {
+        float *dst = hT + ((size_t)unit * DK) * DV;
 #pragma unroll
-        for (int i = 0; i < Cfg::NSW; ++i) {
-            const int id = wave + i * NW;
-            if (id < Cfg::NS_TILES) {
-                const int rt = id / NTV, ct = id % NTV;
-                float *dst = hT + ((size_t)unit * DK) * DV + v0;
+        for (int rt = 0; rt < NTK; ++rt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    dst[(size_t)(rt * 16 + acc_row(lane, r)) * DV + ct * 16 + acc_col(lane)] = Sacc[i][r];
-            }
-        }
+            for (int r = 0; r < 4; ++r)
+                dst[(size_t)(rt * 16 + acc_row(lane, r)) * DV + vc] = Sacc[rt][r];
     }
 }
 

@@ -25,24 +25,20 @@ hipError_t run(const ChunkArgs &a, hipStream_t s) {
     }
 }
 
-// Value-slice width.  Each slice repeats the key-side work (decay factors, Gram
-// matrices, inverse), so wider slices waste less; narrower slices give more
-// workgroups to fill 256 CUs (96 heads x 4 slices of 32 = 384).  32 columns when
-// dv allows it and it fits, else 64, else 16.
-template <class T, int DK, int BV, int C>
-constexpr bool fits(int dv, size_t limit) {
-    return dv % BV == 0 && ChunkCfg<T, DK, BV, C>::kLds <= limit;
-}
+// Value-slice width.  Wave w of a workgroup owns state columns [16w, 16w+16) of
+// its slice, so a 64-column slice keeps all four waves busy in the state chain;
+// the key-side work (decay factors, Gram matrices, inverse) is repeated once per
+// slice.  LDS use does not depend on the slice width.  64 columns when dv allows,
+// else 32, else 16.
 template <class T, int DK, int C>
 constexpr int pick_bv(int dv) {
 #ifdef KDA_CHUNK_BV
     if (dv % KDA_CHUNK_BV == 0 && ChunkCfg<T, DK, KDA_CHUNK_BV, C>::kFits) return KDA_CHUNK_BV;
 #endif
-    const size_t limit = (size_t)160 * 1024;
-    if (fits<T, DK, 32, C>(dv, limit)) return 32;
-    if (fits<T, DK, 64, C>(dv, limit)) return 64;
-    if (fits<T, DK, 16, C>(dv, limit)) return 16;
-    return 0;
+    if (!ChunkCfg<T, DK, 16, C>::kFits) return 0;
+    if (dv % 64 == 0) return 64;
+    if (dv % 32 == 0) return 32;
+    return dv % 16 == 0 ? 16 : 0;
 }
 
 template <class T, class TO, int DK, int C>
@@ -57,21 +53,27 @@ hipError_t run_c(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok) {
     }
 }
 
-// Internal chunk: the requested size or smaller.  The bf16 path prefers 32 tokens:
-// its split products make the intra-chunk work per token grow with the chunk,
-// and the smaller working set fits two workgroups per CU.
+// Internal chunk: the largest of 64, 32, 16 that does not exceed the requested
+// size, fits in LDS and is not above the preferred maximum (KDA_CHUNK_MAX).
+#ifndef KDA_CHUNK_MAX
+#define KDA_CHUNK_MAX 64
+#endif
 template <class T, class TO, int DK>
 hipError_t run_dk(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok) {
     *ok = false;
     hipError_t e = hipErrorNotSupported;
-#ifdef KDA_CHUNK_PREFER32
-    constexpr bool kPrefer32 = KDA_CHUNK_PREFER32;
-#else
-    constexpr bool kPrefer32 = std::is_same<T, bf16>::value;
-#endif
-    if (a.chunk >= 64 && !kPrefer32) { e = run_c<T, TO, DK, 64>(a, s, launch, ok); if (*ok) return e; }
-    if (a.chunk >= 32) { e = run_c<T, TO, DK, 32>(a, s, launch, ok); if (*ok) return e; }
-    if (a.chunk >= 16) { e = run_c<T, TO, DK, 16>(a, s, launch, ok); if (*ok) return e; }
+    if (a.chunk >= 64 && KDA_CHUNK_MAX >= 64) {
+        e = run_c<T, TO, DK, 64>(a, s, launch, ok);
+        if (*ok) return e;
+    }
+    if (a.chunk >= 32 && KDA_CHUNK_MAX >= 32) {
+        e = run_c<T, TO, DK, 32>(a, s, launch, ok);
+        if (*ok) return e;
+    }
+    if (a.chunk >= 16) {
+        e = run_c<T, TO, DK, 16>(a, s, launch, ok);
+        if (*ok) return e;
+    }
     return hipErrorNotSupported;
 }
 
