@@ -42,6 +42,12 @@ __device__ __forceinline__ float group_sum(float v) {
     for (int off = width / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, width);
     return v;
 }
+template <int width>
+__device__ __forceinline__ double group_sum(double v) {
+#pragma unroll
+    for (int off = width / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, width);
+    return v;
+}
 
 // ---------------------------------------------------------------------------
 // 16x16 MFMA tiles.

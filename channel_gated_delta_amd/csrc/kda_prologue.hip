@@ -14,6 +14,15 @@
 // aligned power-of-two group inside the wave, so the L2 sum of squares is a
 // few lane shuffles.  Sequence starts inside a tile switch the out-of-sequence
 // taps to the caller's conv history (or zeros).
+//
+// Rounding.  With bf16 outputs every value is computed in fp64 and rounded
+// once to bf16 (nearest, ties to even), so the result is the correctly rounded
+// conv/SiLU/L2 value; an fp32 evaluation would round a value lying within its
+// own error of a bf16 rounding midpoint to either side, and such 1-ulp flips of
+// q and k move the recurrence's largest outputs by far more than one ulp.  With
+// fp32 outputs the arithmetic is fp32.
+#include <type_traits>
+
 #include "kda_device.cuh"
 #include "kda_launch.h"
 
@@ -28,6 +37,29 @@ __device__ __forceinline__ int64_t seq_off(const int32_t *cu, int i, int64_t tot
     if (!cu) return i == 0 ? 0 : total;
     return min((int64_t)max(cu[i], 0), total);
 }
+
+// Nearest bf16 (ties to even) of a double.  The float conversion rounds first;
+// if that lands exactly on a bf16 midpoint that d itself is not on, the second
+// rounding must go to d's side rather than to the even neighbour.
+__device__ __forceinline__ bf16 bf16_from_f64(double d) {
+    const float f = (float)d;
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0xffffu) == 0x8000u && (double)f != d) {
+        u = (u & 0xffff0000u) + (fabs(d) > fabs((double)f) ? 0x10000u : 0u);
+        return __builtin_bit_cast(bf16, (uint16_t)(u >> 16));
+    }
+    return (bf16)f;
+}
+
+template <class T> struct ConvAcc { typedef float type; };
+template <> struct ConvAcc<bf16> { typedef double type; };
+
+__device__ __forceinline__ float silu_of(float a) { return a / (1.0f + __expf(-a)); }
+__device__ __forceinline__ double silu_of(double a) { return a / (1.0 + exp(-a)); }
+__device__ __forceinline__ float inv_norm(float ss, float eps) { return 1.0f / sqrtf(ss + eps); }
+__device__ __forceinline__ double inv_norm(double ss, float eps) { return 1.0 / sqrt(ss + (double)eps); }
+__device__ __forceinline__ float store_val(float x, float) { return x; }
+__device__ __forceinline__ bf16 store_val(double x, bf16) { return bf16_from_f64(x); }
 
 // Sequence containing token t: the largest n with cu[n] <= t.
 __device__ __forceinline__ int find_seq(const int32_t *cu, int nseq, int64_t t) {
@@ -47,18 +79,19 @@ void conv_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__re
                  const T *__restrict__ hist, int silu, float eps, T *__restrict__ y) {
     constexpr int V = Vec16<T>::n;
     typedef typename Vec16<T>::type VT;
+    typedef typename ConvAcc<T>::type A;
     const int64_t nvec = C / V;
     const int64_t cv = (int64_t)blockIdx.x * kConvThreads + threadIdx.x;  // channel vector
     const bool active = cv < nvec;
     const int64_t c0 = cv * V;
     const int64_t t0 = (int64_t)blockIdx.y * kConvTile;
 
-    float wt[W][V], bs[V];
+    A wt[W][V], bs[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-        bs[e] = (active && bias) ? to_f32(bias[c0 + e]) : 0.f;
+        bs[e] = (active && bias) ? (A)to_f32(bias[c0 + e]) : (A)0;
 #pragma unroll
-        for (int i = 0; i < W; ++i) wt[i][e] = active ? to_f32(w[(c0 + e) * W + i]) : 0.f;
+        for (int i = 0; i < W; ++i) wt[i][e] = active ? (A)to_f32(w[(c0 + e) * W + i]) : (A)0;
     }
 
     // Raw rows t0-(W-1) .. t0+TT-1 (rows outside [0, total) are never used as data).
@@ -85,7 +118,7 @@ void conv_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__re
             bos = seq_off(cu_seqlens, n, total);
             eos = seq_off(cu_seqlens, n + 1, total);
         }
-        float acc[V];
+        A acc[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) acc[e] = bs[e];
 #pragma unroll
@@ -93,31 +126,31 @@ void conv_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__re
             const int64_t p = t - (W - 1) + i;
             if (p >= bos) {
 #pragma unroll
-                for (int e = 0; e < V; ++e) acc[e] += wt[i][e] * to_f32(raw[tt + i][e]);
+                for (int e = 0; e < V; ++e) acc[e] += wt[i][e] * (A)to_f32(raw[tt + i][e]);
             } else if (hist && active) {
                 const T *h = hist + ((int64_t)n * (W - 1) + (p - bos + (W - 1))) * C + c0;
                 const VT hv = *reinterpret_cast<const VT *>(h);
 #pragma unroll
-                for (int e = 0; e < V; ++e) acc[e] += wt[i][e] * to_f32(hv[e]);
+                for (int e = 0; e < V; ++e) acc[e] += wt[i][e] * (A)to_f32(hv[e]);
             }
         }
         if (silu) {
 #pragma unroll
-            for (int e = 0; e < V; ++e) acc[e] = acc[e] / (1.0f + __expf(-acc[e]));
+            for (int e = 0; e < V; ++e) acc[e] = silu_of(acc[e]);
         }
         if constexpr (LPG > 0) {
-            float ss = 0.f;
+            A ss = 0;
 #pragma unroll
             for (int e = 0; e < V; ++e) ss += acc[e] * acc[e];
             ss = group_sum<LPG>(ss);
-            const float inv = 1.0f / sqrtf(ss + eps);
+            const A inv = inv_norm(ss, eps);
 #pragma unroll
             for (int e = 0; e < V; ++e) acc[e] *= inv;
         }
         if (active) {
             VT out;
 #pragma unroll
-            for (int e = 0; e < V; ++e) out[e] = from_f32<T>(acc[e]);
+            for (int e = 0; e < V; ++e) out[e] = store_val(acc[e], T());
             *reinterpret_cast<VT *>(y + t * C + c0) = out;
         }
     }

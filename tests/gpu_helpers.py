@@ -79,6 +79,21 @@ def oracle_prefill(inp, spec, heads):
     return dict(q=q, k=k, v=v, o=o, hT=hT)
 
 
+def assert_prologue(got, ref, dtype):
+    """The prologue's q, k, v against the oracle's: bf16 outputs are the correctly
+    rounded values, so they must be identical; fp32 outputs agree to 1e-5 relative."""
+    for name in ("q", "k", "v"):
+        g, r = np.asarray(got[name], dtype=np.float64), np.asarray(ref[name], dtype=np.float64)
+        if dtype == torch.bfloat16:
+            bad = int(np.sum(g != r))
+            note("  prologue %s: %d of %d bf16 values differ" % (name, bad, g.size))
+            assert bad == 0, "prologue %s: %d values differ from the oracle" % (name, bad)
+        else:
+            err = float(np.max(np.abs(g - r) / (np.abs(r) + 1e-30)))
+            note("  prologue %s: max rel err %.3e" % (name, err))
+            assert err <= 1e-5, "prologue %s: rel err %.3e" % (name, err)
+
+
 def assert_parity(name, got, ref, tol):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

@@ -170,8 +170,14 @@ def test_short_conv_varlen_state(width, dtype):
             ry = oracle.l2norm(ry, D, 1e-6)
         ry = ry.reshape(T, H, D)
         gy = to64(y)
-        bound = eps * np.abs(ry) + 1e-6
-        assert np.all(np.abs(gy - ry) <= bound), "max excess %.3e" % np.max(np.abs(gy - ry) - bound)
+        if dtype == torch.bfloat16:
+            # bf16 outputs are the correctly rounded values: identical to the oracle's rounding
+            rb = oracle.round_bf16(ry)
+            assert np.array_equal(gy, rb), "%d values differ" % int(np.sum(gy != rb))
+        else:
+            bound = eps * np.abs(ry) + 1e-6
+            assert np.all(np.abs(gy - ry) <= bound), \
+                "max excess %.3e" % np.max(np.abs(gy - ry) - bound)
         assert np.array_equal(to64(st_out), rst), "conv history out"
     # in-place history update (state_out aliases conv_state)
     st2 = st.clone()

@@ -13,7 +13,8 @@ import torch
 import channel_gated_delta_amd as kda
 import oracle
 from channel_gated_delta_amd import workloads
-from gpu_helpers import assert_parity, gpu_prefill, note, oracle_prefill, to64, tol_for
+from gpu_helpers import (assert_parity, assert_prologue, gpu_prefill, note, oracle_prefill, to64,
+                         tol_for)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -28,9 +29,12 @@ def run_prefill_workload(name, heads):
     assert bool(torch.isfinite(got["o"]).all()) and bool(torch.isfinite(got["hT"]).all())
     go = to64(got["o"][:, heads])
     gh = to64(got["hT"][:, heads])
+    gp = {name: to64(got[name][:, heads]) for name in ("q", "k", "v")} if spec.conv else None
     del got
     ref = oracle_prefill(inp, spec, heads)
     tol = tol_for(spec.dtype)
+    if gp is not None:
+        assert_prologue(gp, ref, spec.dtype)
     assert_parity("o (sampled heads)", go, ref["o"], tol)
     assert_parity("final state (sampled heads)", gh, ref["hT"], tol)
     return spec
