@@ -375,7 +375,7 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
 
     // ---- registers holding the next chunk's inputs (rows clamped into the sequence)
     VT pq[NQV], pk[NQV];
-    float pv[NTC][4];
+    T pv[NTC][4];            // kept in T: a conversion here would wait for the load
     float pg[RP][2], pb = 0.f;
     auto issue_loads = [&](int64_t cs) {
         const int last = (int)min((int64_t)C, eos - cs) - 1;
@@ -395,7 +395,7 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = min(R * 16 + acc_row(lane, r), last);
-                    pv[R][r] = to_f32(v[(size_t)(cs + t) * rowV + (size_t)h * DV + vc]);
+                    pv[R][r] = v[(size_t)(cs + t) * rowV + (size_t)h * DV + vc];
                 }
         }
         if (fthread) {
@@ -437,7 +437,8 @@ void chunk_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__r
 #pragma unroll
         for (int R = 0; R < NTC; ++R)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) vin[R][r] = (R * 16 + acc_row(lane, r) < nt) ? pv[R][r] : 0.f;
+            for (int r = 0; r < 4; ++r)
+                vin[R][r] = (R * 16 + acc_row(lane, r) < nt) ? to_f32(pv[R][r]) : 0.f;
 
         // cumulative log2-decay of channels 2cp, 2cp+1 over this thread's rows
         float gam[RP][2];
