@@ -36,25 +36,32 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "KDA prefill tokens/s (H=96, d=128) + decode steps/s; % of roofline"
 
 
-def kernel_source_digest() -> str:
-    """Hash of the sources the chunk kernel is built from (to date counter summaries)."""
+KERNEL_SOURCES = {
+    "chunk": ("kda_device.cuh", "kda_chunk.cuh", "kda_chunk_dispatch.cuh", "kda_chunk_bf16.hip"),
+    "decode": ("kda_device.cuh", "kda_decode.hip"),
+}
+
+
+def kernel_source_digest(kind: str) -> str:
+    """Hash of the sources a kernel is built from (to date counter summaries)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "channel_gated_delta_amd", "csrc")
-    for name in ("kda_device.cuh", "kda_chunk.cuh", "kda_chunk_dispatch.cuh", "kda_chunk_bf16.hip"):
+    for name in KERNEL_SOURCES[kind]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kind: str):
-    """HBM bytes per launch from profiles/<kind>_traffic.md if it matches the current source."""
-    path = os.path.join(ROOT, "profiles", "%s_traffic.md" % kind)
+def measured_traffic(kind: str, workload: str):
+    """HBM bytes per launch from profiles/<kind>_<workload>_traffic.md, if that summary was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.md" % (kind, workload))
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"source_digest:\s*([0-9a-f]+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != kernel_source_digest():
+    if not m or not t or m.group(1) != kernel_source_digest(kind):
         return None
     return float(t.group(1))
 
@@ -190,6 +197,18 @@ def cpu_baseline(res, workloads):
                       (n_heads, H, res["T"], dt, H, n_heads)}
 
 
+def copy_calibration(torch, nbytes=1 << 30, reps=3):
+    """A plain copy of known size: every byte read once and written once.  Under a
+    counter profiler its FETCH_SIZE / WRITE_SIZE per dispatch, divided by nbytes,
+    give the factor that turns those counters into bytes."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "dispatches": reps}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,6 +217,9 @@ def main():
     ap.add_argument("--workload", default="prefill", choices=["prefill", "varlen", "long"])
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (torch elementwise kernel), the "
+                         "reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
@@ -214,6 +236,9 @@ def main():
         from channel_gated_delta_amd import build
         build.build()
     kda.library()
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
 
     res = run_prefill(args, torch, kda, workloads)
     spec = res["spec"]
@@ -221,7 +246,7 @@ def main():
     tok_s = T / (res["ms_step"] / 1e3)
     alg_bytes = prefill_step_bytes(T, H, DK, DV, N, spec.h0_std is not None)
     achieved = alg_bytes / (res["chunk_ms"] / 1e3) / 1e9
-    traffic = measured_traffic("chunk_%s" % args.workload)
+    traffic = measured_traffic("chunk", args.workload)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": "chunk_kernel (chunkwise KDA prefill)",
@@ -248,7 +273,7 @@ def main():
                          "roofline": {"bound": "hbm", "achieved": round(dach, 1),
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                       "frac": round(dach / HBM_PEAK_GBS, 4),
-                                      "traffic": measured_traffic("decode"),
+                                      "traffic": measured_traffic("decode", "decode"),
                                       "algorithmic_bytes_per_launch": dbytes}}
     out["prologue_ms_per_step"] = round(res["ms_step"] - res["chunk_ms"], 4)
     out["prologue_bytes_per_step"] = prologue_bytes(T, H, DK)
