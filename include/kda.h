@@ -79,7 +79,9 @@ typedef enum {
  * (weight[c, W-1] multiplies the current token), then y <- y * sigmoid(y) if
  * apply_silu, then, if l2_normalize, every group of head_dim channels of a
  * token is scaled by 1 / sqrt(sum y^2 + l2_eps).  The history restarts at every
- * sequence start.
+ * sequence start.  With bf16 the whole chain is evaluated in fp64 and rounded
+ * once, so every output is the correctly rounded (nearest-even) bf16 value;
+ * with fp32 the arithmetic is fp32.
  *
  *   x              [total_tokens, num_heads * head_dim]   dtype
  *   weight         [num_heads * head_dim, width]           dtype
@@ -130,10 +132,11 @@ KDA_API kda_status_t kda_short_conv(const void *x, const void *weight, const voi
  * Supported: dk, dv in {16, 32, 64, 128}; chunk_size in {16, 32, 64};
  * |q|, |k| entries below 1e3.  The fp32 dtype computes in fp32 throughout; the
  * bf16 dtype runs its products on bf16 matrix cores with fp32 accumulation,
- * keeps the recurrent state in fp32 and uses split (hi + lo) bf16 operands for
- * the products that feed o and the state directly.  When a shape's working set does not fit
- * in a CU's 160 KiB LDS at the requested chunk_size (fp32 with dk = 128), the
- * kernel runs the next smaller chunk size instead.
+ * keeps the recurrent state in fp32 and gives every product split operands
+ * (x = hi + lo, both bf16; three-term products), which keeps the products near
+ * fp32 accuracy.  The internal chunk may be smaller than chunk_size (the
+ * largest of 64, 32, 16 not above it whose working set fits a CU's 160 KiB of
+ * LDS); results do not depend on it beyond rounding.
  */
 KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, const int32_t *cu_seqlens, int32_t num_seqs,
