@@ -37,7 +37,8 @@ METRIC = "KDA prefill tokens/s (H=96, d=128) + decode steps/s; % of roofline"
 
 
 KERNEL_SOURCES = {
-    "chunk": ("kda_device.cuh", "kda_chunk.cuh", "kda_chunk_dispatch.cuh", "kda_chunk_bf16.hip"),
+    "chunk": ("kda_device.cuh", "kda_chunk_common.cuh", "kda_chunk_prep.cuh", "kda_chunk_state.cuh",
+              "kda_chunk_dispatch.cuh", "kda_chunk_bf16.hip"),
     "decode": ("kda_device.cuh", "kda_decode.hip"),
 }
 
@@ -100,6 +101,8 @@ def run_prefill(args, torch, kda, workloads):
     vb = torch.empty((T, H, DV), dtype=spec.dtype, device=dev)
     ob = torch.empty((T, H, DV), dtype=torch.float32, device=dev)
     hT = torch.empty((N, H, DK, DV), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.chunk_workspace_bytes(T, H, DK, DV, spec.chunk, spec.dtype),
+                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -112,7 +115,7 @@ def run_prefill(args, torch, kda, workloads):
             ev[0].record(stream)
         kda.chunk_fwd(qb, kb, vb, inp["g"], inp["beta"], cu_seqlens=cu, scale=spec.read_scale,
                       gate_lower_bound=spec.gate_lb, chunk_size=spec.chunk,
-                      initial_state=inp["h0"], out=ob, final_state=hT)
+                      initial_state=inp["h0"], out=ob, final_state=hT, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
 
@@ -249,7 +252,7 @@ def main():
     traffic = measured_traffic("chunk", args.workload)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "chunk_kernel (chunkwise KDA prefill)",
+            "kernel": "kda_chunk_fwd (chunk_prep_kernel + chunk_state_kernel)",
             "algorithmic_bytes_per_launch": alg_bytes,
             "avg_launch_ms": round(res["chunk_ms"], 4)}
     out = {

@@ -48,10 +48,14 @@ def library() -> ctypes.CDLL:
         lib.kda_short_conv.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp,
                                        _i32, _i32, _f32, _i32, _vp, _vp]
         lib.kda_chunk_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
-                                      _i32, _f32, _f32, _vp, _vp, _vp, _i32, _i32, _vp]
+                                      _i32, _f32, _f32, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                      _i32, _i32, _vp]
+        lib.kda_chunk_fwd_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                     ctypes.POINTER(ctypes.c_size_t)]
         lib.kda_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
                                         _vp, _i32, _i32, _vp]
-        for fn in ("kda_short_conv", "kda_chunk_fwd", "kda_decode_step"):
+        for fn in ("kda_short_conv", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
+                   "kda_decode_step"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_status_string.restype = ctypes.c_char_p
@@ -144,12 +148,13 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               scale: Optional[float] = None, gate_lower_bound: float = -5.0, chunk_size: int = 64,
               initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
               out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-              out_dtype: torch.dtype = torch.float32
+              out_dtype: torch.dtype = torch.float32, workspace: Optional[torch.Tensor] = None
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise KDA prefill.  q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H].
 
     Returns o [T, H, dv] (``out_dtype``, fp32 by default) and the final states
-    [N, H, dk, dv] (fp32) if requested.
+    [N, H, dk, dv] (fp32) if requested.  ``workspace`` (a uint8 GPU tensor of at
+    least ``chunk_workspace_bytes(...)`` bytes) is allocated when not given.
     """
     _dev(q, "q")
     dt = q.dtype
@@ -175,11 +180,26 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     o = out if out is not None else torch.empty((T, H, dv), dtype=out_dtype, device=q.device)
     _dev(o, "out", out_dtype, (T, H, dv))
     sc = dk ** -0.5 if scale is None else float(scale)
+    need = chunk_workspace_bytes(T, H, dk, dv, chunk_size, dt, out_dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", torch.uint8)
     _check(library().kda_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,
         int(chunk_size), sc, float(gate_lower_bound), _ptr(initial_state), _ptr(final_state),
-        _ptr(o), _DTYPES[dt], _DTYPES[out_dtype], _stream(q)))
+        _ptr(o), _ptr(workspace), workspace.numel(), _DTYPES[dt], _DTYPES[out_dtype], _stream(q)))
     return o, final_state
+
+
+def chunk_workspace_bytes(total_tokens: int, num_heads: int, dk: int, dv: int,
+                          chunk_size: int = 64, dtype: torch.dtype = torch.bfloat16,
+                          out_dtype: torch.dtype = torch.float32) -> int:
+    """Device workspace bytes ``chunk_fwd`` needs for these sizes."""
+    n = ctypes.c_size_t(0)
+    _check(library().kda_chunk_fwd_workspace_size(int(total_tokens), int(num_heads), int(dk),
+                                                  int(dv), int(chunk_size), _DTYPES[dtype],
+                                                  _DTYPES[out_dtype], ctypes.byref(n)))
+    return int(n.value)
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

@@ -31,6 +31,53 @@ int vec_elems(kda_dtype_t d) { return d == KDA_DTYPE_BF16 ? 8 : 4; }
 
 }  // namespace
 
+namespace {
+
+kda::ChunkLauncher chunk_launcher(kda_dtype_t dtype, kda_dtype_t out_dtype) {
+    return dtype == KDA_DTYPE_F32       ? kda::launch_chunk_f32
+           : out_dtype == KDA_DTYPE_F32 ? kda::launch_chunk_bf16_f32out
+                                        : kda::launch_chunk_bf16_bf16out;
+}
+
+// Shape checks shared by kda_chunk_fwd and its workspace query; returns the
+// internal chunk size (> 0) or 0 after recording the failure.
+int chunk_shape_check(const char *who, int64_t total_tokens, int32_t num_heads, int32_t dk,
+                      int32_t dv, int32_t chunk_size, kda_dtype_t dtype, kda_dtype_t out_dtype,
+                      kda_status_t *st) {
+    *st = KDA_OK;
+    if (total_tokens < 0 || num_heads < 1 || num_heads > 65535) {
+        *st = fail(KDA_ERR_INVALID_ARG, "%s: bad sizes", who);
+        return 0;
+    }
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) {
+        *st = fail(KDA_ERR_INVALID_ARG, "%s: bad dtype", who);
+        return 0;
+    }
+    if (dtype == KDA_DTYPE_F32 && out_dtype != KDA_DTYPE_F32) {
+        *st = fail(KDA_ERR_UNSUPPORTED, "%s: fp32 inputs need an fp32 output", who);
+        return 0;
+    }
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) {
+        *st = fail(KDA_ERR_UNSUPPORTED, "%s: dk/dv not in {16,32,64,128}", who);
+        return 0;
+    }
+    if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) {
+        *st = fail(KDA_ERR_UNSUPPORTED, "%s: chunk_size not in {16,32,64}", who);
+        return 0;
+    }
+    kda::ChunkArgs probe{};
+    probe.heads = num_heads;
+    probe.dk = dk;
+    probe.dv = dv;
+    probe.chunk = chunk_size;
+    int c = 0;
+    (void)chunk_launcher(dtype, out_dtype)(probe, nullptr, false, &c);
+    if (c == 0) *st = fail(KDA_ERR_UNSUPPORTED, "%s: no kernel for dk=%d dv=%d", who, dk, dv);
+    return c;
+}
+
+}  // namespace
+
 extern "C" {
 
 KDA_API const char *kda_status_string(kda_status_t s) {
@@ -81,44 +128,57 @@ KDA_API kda_status_t kda_short_conv(const void *x, const void *weight, const voi
                     "kda_short_conv");
 }
 
+KDA_API kda_status_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_heads,
+                                                  int32_t dk, int32_t dv, int32_t chunk_size,
+                                                  kda_dtype_t dtype, kda_dtype_t out_dtype,
+                                                  size_t *bytes) {
+    g_last_error[0] = '\0';
+    if (!bytes) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd_workspace_size: NULL bytes");
+    kda_status_t st;
+    const int c = chunk_shape_check("kda_chunk_fwd_workspace_size", total_tokens, num_heads, dk,
+                                    dv, chunk_size, dtype, out_dtype, &st);
+    if (c == 0) return st;
+    *bytes = kda::chunk_workspace_bytes(total_tokens, num_heads, c);
+    return KDA_OK;
+}
+
 KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, const int32_t *cu_seqlens, int32_t num_seqs,
                                    int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
                                    int32_t chunk_size, float scale, float gate_lower_bound,
                                    const float *initial_state, float *final_state, void *o,
-                                   kda_dtype_t dtype, kda_dtype_t out_dtype, void *stream) {
+                                   void *workspace, size_t workspace_bytes, kda_dtype_t dtype,
+                                   kda_dtype_t out_dtype, void *stream) {
     g_last_error[0] = '\0';
-    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o))
-        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: NULL q/k/v/g/beta/o");
-    if (num_seqs < 1 || total_tokens < 0 || num_heads < 1)
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o || !workspace))
+        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: NULL q/k/v/g/beta/o/workspace");
+    if (num_seqs < 1)
         return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: bad sizes");
     if (!cu_seqlens && num_seqs != 1)
         return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: cu_seqlens NULL needs num_seqs == 1");
-    if (!valid_dtype(dtype) || !valid_dtype(out_dtype))
-        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: bad dtype");
-    if (dtype == KDA_DTYPE_F32 && out_dtype != KDA_DTYPE_F32)
-        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: fp32 inputs need an fp32 output");
     if (!isfinite(scale)) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: scale not finite");
-    if (o && (o == q || o == k || o == v || o == (const void *)g || o == (const void *)beta))
-        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: o aliases an input");
+    if (o && (o == q || o == k || o == v || o == (const void *)g || o == (const void *)beta ||
+              o == workspace))
+        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: o aliases an input or the workspace");
     if (!(gate_lower_bound <= 0.f)) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: gate bound > 0 or NaN");
     if (gate_lower_bound < -9.f)
         return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: gate_lower_bound below -9");
-    if (!head_dim_ok(dk) || !head_dim_ok(dv))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: dk/dv not in {16,32,64,128}");
-    if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
-        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: chunk_size not in {16,32,64}");
-    if ((int64_t)num_seqs * num_heads * (dv / 16) > ((int64_t)1 << 28))
+    kda_status_t st;
+    const int c = chunk_shape_check("kda_chunk_fwd", total_tokens, num_heads, dk, dv, chunk_size,
+                                    dtype, out_dtype, &st);
+    if (c == 0) return st;
+    if ((int64_t)num_seqs * num_heads * (dv / 16) > ((int64_t)1 << 28) ||
+        (total_tokens + c - 1) / c > ((int64_t)1 << 31) - 1)
         return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: grid too large");
+    if (total_tokens > 0 && workspace_bytes < kda::chunk_workspace_bytes(total_tokens, num_heads, c))
+        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: workspace of %zu bytes, %zu needed",
+                    workspace_bytes, kda::chunk_workspace_bytes(total_tokens, num_heads, c));
     kda::ChunkArgs a{q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, dk, dv,
-                     chunk_size, scale, gate_lower_bound, initial_state, final_state, o};
-    auto launcher = dtype == KDA_DTYPE_F32            ? kda::launch_chunk_f32
-                    : out_dtype == KDA_DTYPE_F32      ? kda::launch_chunk_bf16_f32out
-                                                      : kda::launch_chunk_bf16_bf16out;
-    bool ok = false;
-    (void)launcher(a, (hipStream_t)stream, false, &ok);
-    if (!ok) return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: no kernel for dk=%d dv=%d", dk, dv);
-    return from_hip(launcher(a, (hipStream_t)stream, true, &ok), "kda_chunk_fwd");
+                     chunk_size, scale, gate_lower_bound, initial_state, final_state, o,
+                     (float *)workspace};
+    int used = 0;
+    return from_hip(chunk_launcher(dtype, out_dtype)(a, (hipStream_t)stream, true, &used),
+                    "kda_chunk_fwd");
 }
 
 KDA_API kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const float *g,

@@ -3,7 +3,7 @@
 #include "kda_chunk_dispatch.cuh"
 
 namespace kda {
-hipError_t launch_chunk_bf16_f32out(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok) {
-    return chunk_detail::dispatch<bf16, float>(a, s, launch, ok);
+hipError_t launch_chunk_bf16_f32out(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used) {
+    return chunk_detail::dispatch<bf16, float>(a, s, launch, chunk_used);
 }
 }  // namespace kda

@@ -1,0 +1,231 @@
+// kda_chunk_common.cuh -- pieces shared by the two chunk kernels of the KDA
+// prefill (kda_chunk_prep.cuh, kda_chunk_state.cuh).
+//
+// Semantics: the token recurrence of [Walkthrough] 第三站-第五站 (decay the rows
+// of S by exp(g_t), predict S^T k_t, write beta_t k_t (v_t - S^T k_t)^T, read
+// scale * S^T q_t), executed chunk by chunk ([Walkthrough] 彩蛋: chunks pass the
+// state, the work inside a chunk becomes matrix products; [Replication-2] 图1:
+// transitions compose into one chunk-level transform).
+//
+// Chunk algebra (derived from the recurrence; state S0 entering a chunk of n
+// tokens, G_t = sum_{j<=t} g_j per key channel, exponentials of differences only):
+//   A_ti = sum_c k_tc k_ic e^{G_tc - G_ic}  (i < t),   P_ti = sum_c q_tc k_ic e^{G_tc - G_ic}  (i <= t)
+//   Tb   = (I + diag(beta) A)^{-1} diag(beta)
+//   U    = Tb (V - (K * e^{G}) S0)
+//   O    = scale (Q * e^{G}) S0 + scale P U
+//   S    = diag(e^{G_n}) S0 + (K * e^{G_n - G})^T U
+// Tb and scale*P depend on q, k, g, beta of the chunk only, not on the state, so
+// a first kernel computes them for every (chunk, head) at once (fully parallel)
+// and a second kernel walks the chunks of each sequence with the state on chip.
+//
+// Precision.  The outputs are heavy-tailed (the largest |o| is 10-30x the rms),
+// so one bf16 rounding of a product operand already costs ~2^-9 * 30 of the rms.
+// With bf16 inputs every product therefore uses split operands x = hi + lo
+// (both bf16, |lo| <= 2^-9 |x|) and the three-term product hi*hi + hi*lo + lo*hi
+// (~2^-16 relative); the diagonal of P (the token's own term, scale q_t . k_t)
+// is computed exactly in fp32.  With fp32 inputs the products run on fp32 MFMA.
+#pragma once
+
+#include <type_traits>
+
+#include "kda_device.cuh"
+
+namespace kda {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two adjacent elements of T.
+template <class T> struct Pair;
+template <> struct Pair<bf16> { typedef bf16x2 type; };
+template <> struct Pair<float> { typedef f32x2 type; };
+
+// Packed-sequence offset i clamped to [0, total]; cu == NULL is one sequence.
+__device__ __forceinline__ int64_t chunk_seq_off(const int32_t *cu, int i, int64_t total) {
+    if (!cu) return i == 0 ? 0 : total;
+    return min((int64_t)max(cu[i], 0), total);
+}
+
+__device__ __forceinline__ void split2(float x, bf16 &hh, bf16 &ll) {
+    hh = (bf16)x;
+    ll = (bf16)(x - (float)hh);
+}
+
+// Store x0, x1 at H[i], H[i+1] (and the low parts at L[i], L[i+1] when T is bf16).
+template <class T>
+__device__ __forceinline__ void put2(T *H, T *L, int i, float x0, float x1) {
+    typedef typename Pair<T>::type P2;
+    if constexpr (std::is_same<T, bf16>::value) {
+        bf16 h0, l0, h1, l1;
+        split2(x0, h0, l0);
+        split2(x1, h1, l1);
+        P2 h, l;
+        h[0] = h0; h[1] = h1;
+        l[0] = l0; l[1] = l1;
+        *reinterpret_cast<P2 *>(H + i) = h;
+        *reinterpret_cast<P2 *>(L + i) = l;
+    } else {
+        *reinterpret_cast<P2 *>(H + i) = P2{x0, x1};
+    }
+}
+template <class T>
+__device__ __forceinline__ void put1(T *H, T *L, int i, float x) {
+    if constexpr (std::is_same<T, bf16>::value) {
+        split2(x, H[i], L[i]);
+    } else {
+        H[i] = x;
+    }
+}
+
+template <class F>
+__device__ __forceinline__ void scale_frag(F &f, const float *s) {
+    if constexpr (std::is_same<F, float>::value) {
+        f *= s[0];
+    } else {
+        constexpr int n = sizeof(F) / sizeof(bf16);
+#pragma unroll
+        for (int e = 0; e < n; ++e) f[e] = (bf16)((float)f[e] * s[e]);
+    }
+}
+
+// (hi + lo) * s re-split into a new (hi, lo) pair, in fp32.
+template <class F>
+__device__ __forceinline__ void rescale_split(F &hi, F &lo, const float *s) {
+    constexpr int n = sizeof(F) / sizeof(bf16);
+#pragma unroll
+    for (int e = 0; e < n; ++e) {
+        const float x = ((float)hi[e] + (float)lo[e]) * s[e];
+        const bf16 hh = (bf16)x;
+        hi[e] = hh;
+        lo[e] = (bf16)(x - (float)hh);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Products whose B operand is an accumulator tile held in registers.
+//
+// An accumulator tile holds B[(l >> 4) * 4 + r][l & 15] in element r of lane l.
+// For a 32-row k block made of two such tiles (a: rows 0-15, b: rows 16-31), the
+// lane's 8 B values are rows {(l>>4)*4 + 0..3} of a and of b; the hardware pairs
+// A and B entries by (lane group, element), so the A fragment is read with the
+// same k order: A[row][k0 + (l>>4)*4 + 0..3] and A[row][k0 + 16 + (l>>4)*4 + 0..3].
+// A 16-row block uses the 16x16x16 instruction with one tile.  fp32 uses four
+// 16x16x4 steps per 16-row block, step s taking element s.
+// ---------------------------------------------------------------------------
+struct BReg8 { bf16x8 h, l; };
+struct BReg4 { bf16x4 h, l; };
+
+__device__ __forceinline__ BReg8 breg8(const f32x4 &a, const f32x4 &b) {
+    BReg8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf16 hh, ll;
+        split2(a[e], hh, ll); r.h[e] = hh; r.l[e] = ll;
+        split2(b[e], hh, ll); r.h[e + 4] = hh; r.l[e + 4] = ll;
+    }
+    return r;
+}
+__device__ __forceinline__ BReg4 breg4(const f32x4 &a) {
+    BReg4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf16 hh, ll;
+        split2(a[e], hh, ll); r.h[e] = hh; r.l[e] = ll;
+    }
+    return r;
+}
+
+// A fragments (hi, lo) from bf16 LDS matrices [rows][ld], permuted k order.
+__device__ __forceinline__ void afrag8(const bf16 *Mh, const bf16 *Ml, int ld, int row0, int k0,
+                                       int lane, bf16x8 &hh, bf16x8 &ll) {
+    const int off = (row0 + (lane & 15)) * ld + k0 + (lane >> 4) * 4;
+    const bf16x4 h0 = *reinterpret_cast<const bf16x4 *>(Mh + off);
+    const bf16x4 h1 = *reinterpret_cast<const bf16x4 *>(Mh + off + 16);
+    const bf16x4 l0 = *reinterpret_cast<const bf16x4 *>(Ml + off);
+    const bf16x4 l1 = *reinterpret_cast<const bf16x4 *>(Ml + off + 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        hh[e] = h0[e]; hh[e + 4] = h1[e];
+        ll[e] = l0[e]; ll[e + 4] = l1[e];
+    }
+}
+__device__ __forceinline__ void afrag4(const bf16 *Mh, const bf16 *Ml, int ld, int row0, int k0,
+                                       int lane, bf16x4 &hh, bf16x4 &ll) {
+    const int off = (row0 + (lane & 15)) * ld + k0 + (lane >> 4) * 4;
+    hh = *reinterpret_cast<const bf16x4 *>(Mh + off);
+    ll = *reinterpret_cast<const bf16x4 *>(Ml + off);
+}
+
+__device__ __forceinline__ f32x4 mma3(const bf16x8 &ah, const bf16x8 &al, const BReg8 &bb,
+                                      f32x4 c) {
+    c = mma(ah, bb.h, c);
+    c = mma(ah, bb.l, c);
+    return mma(al, bb.h, c);
+}
+__device__ __forceinline__ f32x4 mma3(const bf16x4 &ah, const bf16x4 &al, const BReg4 &bb,
+                                      f32x4 c) {
+    c = mma(ah, bb.h, c);
+    c = mma(ah, bb.l, c);
+    return mma(al, bb.h, c);
+}
+
+// D += A[row0.., 0..16*nb) * B, with B given as NBLK 16-row accumulator tiles
+// (prepared once, used for several products) and A from (hi, lo) matrices of T
+// in LDS (bf16: three-term split products; fp32: Ml unused, fp32 MFMA).
+template <class T, int NBLK>
+struct RegB {
+    BReg8 b8[NBLK / 2 > 0 ? NBLK / 2 : 1];
+    BReg4 b4;
+    const f32x4 *tiles;
+    __device__ __forceinline__ void prepare(const f32x4 *t) {
+        tiles = t;
+        if constexpr (std::is_same<T, bf16>::value) {
+#pragma unroll
+            for (int j = 0; j < NBLK / 2; ++j) b8[j] = breg8(t[2 * j], t[2 * j + 1]);
+            if constexpr (NBLK % 2) b4 = breg4(t[NBLK - 1]);
+        }
+    }
+    __device__ __forceinline__ f32x4 mul(f32x4 acc, const T *Mh, const T *Ml, int ld, int row0,
+                                         int nb, int lane) const {
+        if constexpr (std::is_same<T, bf16>::value) {
+#pragma unroll
+            for (int j = 0; j < NBLK / 2; ++j) {
+                if (2 * j < nb) {
+                    if (2 * j + 1 < nb) {
+                        bf16x8 ah, al;
+                        afrag8(Mh, Ml, ld, row0, 32 * j, lane, ah, al);
+                        acc = mma3(ah, al, b8[j], acc);
+                    } else {   // only the first tile of this pair is inside the range
+                        bf16x4 ah, al;
+                        afrag4(Mh, Ml, ld, row0, 32 * j, lane, ah, al);
+                        BReg4 bb;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { bb.h[e] = b8[j].h[e]; bb.l[e] = b8[j].l[e]; }
+                        acc = mma3(ah, al, bb, acc);
+                    }
+                }
+            }
+            if constexpr (NBLK % 2) {
+                if (NBLK - 1 < nb) {
+                    bf16x4 ah, al;
+                    afrag4(Mh, Ml, ld, row0, 16 * (NBLK - 1), lane, ah, al);
+                    acc = mma3(ah, al, b4, acc);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NBLK; ++j) {
+                if (j < nb) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int col = 16 * j + (lane >> 4) * 4 + s;
+                        acc = mma(Mh[(row0 + (lane & 15)) * ld + col], tiles[j][s], acc);
+                    }
+                }
+            }
+        }
+        return acc;
+    }
+};
+
+}  // namespace kda

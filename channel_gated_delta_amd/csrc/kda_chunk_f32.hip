@@ -2,7 +2,7 @@
 #include "kda_chunk_dispatch.cuh"
 
 namespace kda {
-hipError_t launch_chunk_f32(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok) {
-    return chunk_detail::dispatch<float, float>(a, s, launch, ok);
+hipError_t launch_chunk_f32(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used) {
+    return chunk_detail::dispatch<float, float>(a, s, launch, chunk_used);
 }
 }  // namespace kda

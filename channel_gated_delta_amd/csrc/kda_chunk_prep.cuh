@@ -1,0 +1,329 @@
+// kda_chunk_prep.cuh -- first kernel of the chunkwise KDA prefill: for every
+// (chunk, head) at once, Tb = (I + diag(beta) A)^{-1} diag(beta) and scale * P
+// (chunk algebra in kda_chunk_common.cuh).  These depend on q, k, g, beta of the
+// chunk only, so the whole batch is one parallel grid; the sequential kernel
+// (kda_chunk_state.cuh) reads them back.
+//
+// Output (workspace, fp32): row t of a chunk starting at token cs is stored at
+// tb[(t * H + h) * C + i] (i = 0..C-1, column i is token cs + i; zero for i > t)
+// and likewise scale * P (its diagonal scale * q_t . k_t exact in fp32).
+//
+// Decay numerics ([Walkthrough] 彩蛋: products of retention factors and their
+// reciprocals must stay inside the floating-point range).  A and P factor
+// e^{G_t - G_i} through 16-token sub-tiles.  Diagonal tiles use the tile's middle
+// row m as reference: rows e^{G_t - G_m}, columns e^{G_m - G_i}, both within
+// e^{+-8|lb|}; a column factor can only underflow (< e^-87) where the lost term is
+// below e^{-87 + 8|lb|}, negligible for lb >= -9.  Off-diagonal pairs (R, I < R)
+// use the first row s of tile R: rows e^{G_t - G_s} (the middle-referenced row
+// operand times e^{G_m - G_s}) and columns e^{G_s - G_i} (the middle-referenced
+// column operand of tile I times e^{G_s - G_{m_I}}); both factors are <= 1, so
+// any underflow means a negligible product.  Exponents are in log2 units.
+//
+// Work decomposition: one workgroup (4 waves) per (C-token tile of the packed
+// batch, head); it handles the chunk (if any) of every sequence whose chunk
+// start lies in its tile.  Thread (cp, part) owns key channels 2cp, 2cp+1 of the
+// rows [part*RP, part*RP + RP) for the decay phase; the Gram tiles run on MFMA,
+// the 16x16 diagonal blocks of the inverse by forward substitution (one lane per
+// column) and the off-diagonal blocks by fp32 MFMA block substitution.
+#pragma once
+
+#include "kda_chunk_common.cuh"
+
+namespace kda {
+
+template <class T, int DK_, int C_>
+struct PrepCfg {
+    static constexpr int DK = DK_, C = C_;
+    static constexpr bool kSplit = std::is_same<T, bf16>::value;
+    static constexpr int NSPLIT = kSplit ? 2 : 1;
+    static constexpr int NW = 4, NT = NW * kWave;
+    static constexpr int NTC = C / 16;
+    static constexpr int PAD = 16 / (int)sizeof(T);
+    static constexpr int LDK = DK + PAD;                        // [C][DK] operand rows
+    static constexpr int LDA = C + 4;                           // fp32 [C][C] rows
+    static constexpr int KPL_DK = KplFor<T, DK>::value;
+    static constexpr int NPAIR = NTC * (NTC - 1) / 2;
+    static constexpr int NPC = DK / 2;                          // channel pairs
+    static constexpr int NPART = (NT / NPC) < C ? (NT / NPC) : C;
+    static constexpr int RP = C / NPART;                        // rows per part
+    static_assert(NPART * RP == C && NPC <= kWave, "shape");
+
+    static constexpr size_t al(size_t x) { return (x + 15) & ~(size_t)15; }
+    static constexpr size_t szCK = al((size_t)C * LDK * sizeof(T));
+    static constexpr size_t szCC = al((size_t)C * LDA * 4);
+    static constexpr size_t szY = al((size_t)(NTC > 1 ? NTC - 1 : 1) * 256 * 4);
+    static constexpr size_t szSmall =
+        al((size_t)(2 * C + (NPAIR > 0 ? NPAIR : 1) * DK + (3 * NTC + NPART) * DK) * 4);
+    static constexpr size_t oGram = 0;                              // q*Dr, k*Dr, k*Dc (hi, lo)
+    static constexpr size_t oA = oGram + 3 * NSPLIT * szCK;         // A -> Tb (fp32)
+    static constexpr size_t oP = oA + szCC;                         // scale * P (fp32)
+    static constexpr size_t oY = oP + szCC;
+    static constexpr size_t oSmall = oY + szY;
+    static constexpr size_t kLds = oSmall + szSmall;
+    static constexpr bool kFits = kLds <= 160 * 1024;
+    static constexpr int kMinWg = kLds <= 53 * 1024 ? 3 : (kLds <= 80 * 1024 ? 2 : 1);
+};
+
+template <class T, int DK, int C>
+__global__ __launch_bounds__(256, (PrepCfg<T, DK, C>::kMinWg))
+void chunk_prep_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                       const float *__restrict__ g, const float *__restrict__ beta,
+                       const int32_t *__restrict__ cu_seqlens, int nseq, int64_t total, int H,
+                       float scale, float *__restrict__ tb_out, float *__restrict__ p_out) {
+    using Cfg = PrepCfg<T, DK, C>;
+    constexpr bool SPLIT = Cfg::kSplit;
+    constexpr int NW = Cfg::NW, NT = Cfg::NT, NTC = Cfg::NTC;
+    constexpr int LDK = Cfg::LDK, LDA = Cfg::LDA, KPL_DK = Cfg::KPL_DK;
+    constexpr int NPC = Cfg::NPC, NPART = Cfg::NPART, RP = Cfg::RP;
+    typedef typename Pair<T>::type T2;
+
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::kLds];
+    constexpr size_t CKE = Cfg::szCK / sizeof(T);
+    T *sQDh = reinterpret_cast<T *>(smem + Cfg::oGram);
+    T *sKDh = sQDh + Cfg::NSPLIT * CKE;
+    T *sKCh = sKDh + Cfg::NSPLIT * CKE;
+    T *sQDl = sQDh + (SPLIT ? CKE : 0);
+    T *sKDl = sKDh + (SPLIT ? CKE : 0);
+    T *sKCl = sKCh + (SPLIT ? CKE : 0);
+    float *sA = reinterpret_cast<float *>(smem + Cfg::oA);
+    float *sPf = reinterpret_cast<float *>(smem + Cfg::oP);
+    float *sY = reinterpret_cast<float *>(smem + Cfg::oY);
+    float *sBeta = reinterpret_cast<float *>(smem + Cfg::oSmall);
+    float *sPd = sBeta + C;                                            // scale q_t . k_t
+    float *sBnd = sPd + C;                                             // e^{G_sR - G_mI}, I < R
+    float *sGm = sBnd + (Cfg::NPAIR > 0 ? Cfg::NPAIR : 1) * DK;        // G at tile middles
+    float *sGs = sGm + NTC * DK;                                       // G at tile first rows
+    float *sRsc = sGs + NTC * DK;                                      // e^{G_mR - G_sR}
+    float *sTot = sRsc + NTC * DK;                                     // part sums of g
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int h = blockIdx.y;
+    const int64_t t0 = (int64_t)blockIdx.x * C, t1 = min(t0 + C, total);
+    const size_t rowQK = (size_t)H * DK;
+    const int cp = tid % NPC, part = tid / NPC;
+    const bool fthread = part < NPART;
+
+    // The sequences overlapping [t0, t1): the first is the last n with cu[n] <= t0.
+    int n = 0;
+    if (cu_seqlens) {
+        int lo = 0, hi = nseq - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (chunk_seq_off(cu_seqlens, mid, total) <= t0) lo = mid; else hi = mid - 1;
+        }
+        n = lo;
+    }
+    bool first = true;
+    for (; n < nseq; ++n) {
+        const int64_t bos = chunk_seq_off(cu_seqlens, n, total);
+        if (bos >= t1) break;
+        const int64_t eos = max(chunk_seq_off(cu_seqlens, n + 1, total), bos);
+        // this sequence's chunk start inside [t0, t1), if any
+        const int64_t cs = bos >= t0 ? bos : bos + ((t0 - bos + C - 1) / C) * C;
+        if (cs >= t1 || cs >= eos) continue;
+        const int nt = (int)min((int64_t)C, eos - cs);
+        if (!first) __syncthreads();   // the previous chunk's LDS reads are done
+        first = false;
+
+        // ---- loads and the in-chunk cumulative log2-decay (rows >= nt are zero)
+        float qv[RP][2], kv[RP][2], gam[RP][2];
+        if (fthread) {
+            T2 qr[RP], kr[RP];
+            f32x2 gr[RP];
+#pragma unroll
+            for (int j = 0; j < RP; ++j) {
+                const int r = min(part * RP + j, nt - 1);
+                const size_t off = (size_t)(cs + r) * rowQK + (size_t)h * DK + 2 * cp;
+                qr[j] = *reinterpret_cast<const T2 *>(q + off);
+                kr[j] = *reinterpret_cast<const T2 *>(k + off);
+                gr[j] = *reinterpret_cast<const f32x2 *>(g + off);
+            }
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int j = 0; j < RP; ++j) {
+                const bool in = part * RP + j < nt;
+                qv[j][0] = in ? to_f32(qr[j][0]) : 0.f;
+                qv[j][1] = in ? to_f32(qr[j][1]) : 0.f;
+                kv[j][0] = in ? to_f32(kr[j][0]) : 0.f;
+                kv[j][1] = in ? to_f32(kr[j][1]) : 0.f;
+                a0 += (in ? gr[j][0] : 0.f) * kLog2e;
+                a1 += (in ? gr[j][1] : 0.f) * kLog2e;
+                gam[j][0] = a0;
+                gam[j][1] = a1;
+                // exact diagonal of P: scale * q_r . k_r over the NPC lanes of this part
+                const float dot = group_sum<NPC>(qv[j][0] * kv[j][0] + qv[j][1] * kv[j][1]);
+                if (cp == 0) sPd[part * RP + j] = scale * dot;
+            }
+            sTot[part * DK + 2 * cp] = a0;
+            sTot[part * DK + 2 * cp + 1] = a1;
+        }
+        if (tid < C) sBeta[tid] = tid < nt ? beta[(size_t)(cs + tid) * H + h] : 0.f;
+        __syncthreads();
+        if (fthread) {
+            float o0 = 0.f, o1 = 0.f;
+            for (int p = 0; p < part; ++p) {
+                o0 += sTot[p * DK + 2 * cp];
+                o1 += sTot[p * DK + 2 * cp + 1];
+            }
+#pragma unroll
+            for (int j = 0; j < RP; ++j) {
+                gam[j][0] += o0;
+                gam[j][1] += o1;
+                const int r = part * RP + j;
+                if ((r & 15) == 8) {
+                    sGm[(r >> 4) * DK + 2 * cp] = gam[j][0];
+                    sGm[(r >> 4) * DK + 2 * cp + 1] = gam[j][1];
+                }
+                if ((r & 15) == 0) {
+                    sGs[(r >> 4) * DK + 2 * cp] = gam[j][0];
+                    sGs[(r >> 4) * DK + 2 * cp + 1] = gam[j][1];
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- Gram operands (hi, lo): q e^{G_t-G_m}, k e^{G_t-G_m}, k e^{G_m-G_t}
+        if (fthread) {
+#pragma unroll
+            for (int j = 0; j < RP; ++j) {
+                const int r = part * RP + j;
+                float dr[2], dc[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float d = gam[j][e] - sGm[(r >> 4) * DK + 2 * cp + e];
+                    dr[e] = exp2_clamped(d);
+                    dc[e] = exp2_clamped(-d);
+                }
+                const int i = r * LDK + 2 * cp;
+                put2(sQDh, sQDl, i, qv[j][0] * dr[0], qv[j][1] * dr[1]);
+                put2(sKDh, sKDl, i, kv[j][0] * dr[0], kv[j][1] * dr[1]);
+                put2(sKCh, sKCl, i, kv[j][0] * dc[0], kv[j][1] * dc[1]);
+            }
+        }
+        if (tid < DK) {
+            const int c = tid;
+#pragma unroll
+            for (int R = 1; R < NTC; ++R) {
+                sRsc[R * DK + c] = exp2_clamped(sGm[R * DK + c] - sGs[R * DK + c]);
+#pragma unroll
+                for (int I = 0; I < R; ++I)
+                    sBnd[(R * (R - 1) / 2 + I) * DK + c] =
+                        exp2_clamped(sGs[R * DK + c] - sGm[I * DK + c]);
+            }
+        }
+        __syncthreads();
+
+        // ---- Gram tiles A (strict lower) and scale * P (lower, exact diagonal)
+        for (int p = wave; p < NTC * NTC; p += NW) {
+            const int R = p / NTC, I = p % NTC;
+            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+            if (I <= R) {
+                const float *bnd = sBnd + (I < R ? (R * (R - 1) / 2 + I) * DK : 0);
+                const float *rsc = sRsc + R * DK;
+                for (int k0 = 0; k0 < DK; k0 += 4 * KPL_DK) {
+                    auto kh = load_frag<T, KPL_DK>(sKDh, LDK, R * 16, k0, lane);
+                    auto qh = load_frag<T, KPL_DK>(sQDh, LDK, R * 16, k0, lane);
+                    auto ch = load_frag<T, KPL_DK>(sKCh, LDK, I * 16, k0, lane);
+                    if constexpr (SPLIT) {
+                        auto kl = load_frag<T, KPL_DK>(sKDl, LDK, R * 16, k0, lane);
+                        auto ql = load_frag<T, KPL_DK>(sQDl, LDK, R * 16, k0, lane);
+                        auto cl = load_frag<T, KPL_DK>(sKCl, LDK, I * 16, k0, lane);
+                        if (I < R) {   // re-reference rows and columns to s_R
+                            const int kk = k0 + (lane >> 4) * KPL_DK;
+                            rescale_split(kh, kl, rsc + kk);
+                            rescale_split(qh, ql, rsc + kk);
+                            rescale_split(ch, cl, bnd + kk);
+                        }
+                        accA = mma(kh, cl, accA);
+                        accA = mma(kl, ch, accA);
+                        accP = mma(qh, cl, accP);
+                        accP = mma(ql, ch, accP);
+                    } else {
+                        if (I < R) {
+                            const int kk = k0 + (lane >> 4) * KPL_DK;
+                            scale_frag(kh, rsc + kk);
+                            scale_frag(qh, rsc + kk);
+                            scale_frag(ch, bnd + kk);
+                        }
+                    }
+                    accA = mma(kh, ch, accA);
+                    accP = mma(qh, ch, accP);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = R * 16 + acc_row(lane, r), col = I * 16 + acc_col(lane);
+                sA[row * LDA + col] = row > col ? accA[r] : 0.f;
+                sPf[row * LDA + col] = row > col ? scale * accP[r] : (row == col ? sPd[row] : 0.f);
+            }
+        }
+        __syncthreads();
+
+        // ---- Tb = (I + diag(beta) A)^{-1} diag(beta)
+        // diagonal 16x16 blocks: lane i builds column i by forward substitution
+        for (int R = wave; R < NTC; R += NW) {
+            const int i = lane;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float br = sBeta[R * 16 + r];
+                float s = 0.f;
+#pragma unroll
+                for (int m2 = 0; m2 < r; ++m2) s += sA[(R * 16 + r) * LDA + R * 16 + m2] * x[m2];
+                x[r] = (r == i) ? 1.f : (r < i ? 0.f : -br * s);
+            }
+            if (i < 16) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sA[(R * 16 + r) * LDA + R * 16 + i] = x[r];
+            }
+        }
+        __syncthreads();
+        // off-diagonal blocks, one block row at a time (fp32 MFMA)
+        for (int R = 1; R < NTC; ++R) {
+            // Y_I = sum_{M=I}^{R-1} diag(beta_R) A_RM X_MI
+            for (int I = wave; I < R; I += NW) {
+                f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                const float br = sBeta[R * 16 + (lane & 15)];
+                for (int k0 = I * 16; k0 < R * 16; k0 += 4) {
+                    const float a = br * sA[(R * 16 + (lane & 15)) * LDA + k0 + (lane >> 4)];
+                    const float bb = sA[(k0 + (lane >> 4)) * LDA + I * 16 + (lane & 15)];
+                    y = mma(a, bb, y);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sY[I * 256 + acc_row(lane, r) * 16 + acc_col(lane)] = y[r];
+            }
+            __syncthreads();
+            // X_RI = -X_RR Y_I
+            for (int I = wave; I < R; I += NW) {
+                f32x4 xx = {0.f, 0.f, 0.f, 0.f};
+                for (int k0 = 0; k0 < 16; k0 += 4) {
+                    const float a = sA[(R * 16 + (lane & 15)) * LDA + R * 16 + k0 + (lane >> 4)];
+                    const float bb = sY[I * 256 + (k0 + (lane >> 4)) * 16 + (lane & 15)];
+                    xx = mma(a, bb, xx);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sA[(R * 16 + acc_row(lane, r)) * LDA + I * 16 + acc_col(lane)] = -xx[r];
+            }
+            __syncthreads();
+        }
+
+        // ---- write Tb = X diag(beta) and scale * P, rows < nt, 4 columns per item
+        for (int idx = tid; idx < C * C / 4; idx += NT) {
+            const int r = (idx * 4) / C, c0 = (idx * 4) % C;
+            if (r < nt) {
+                f32x4 tv, pv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    tv[e] = sA[r * LDA + c0 + e] * sBeta[c0 + e];
+                    pv[e] = sPf[r * LDA + c0 + e];
+                }
+                const size_t o = ((size_t)(cs + r) * H + h) * C + c0;
+                *reinterpret_cast<f32x4 *>(tb_out + o) = tv;
+                *reinterpret_cast<f32x4 *>(p_out + o) = pv;
+            }
+        }
+    }
+}
+
+}  // namespace kda

@@ -30,7 +30,13 @@ struct ChunkArgs {
     const float *h0;
     float *hT;
     void *o;        // output dtype chosen by the launcher called
+    float *workspace;   // 2 * total_tokens * heads * C floats (C = the internal chunk)
 };
+
+// Workspace of the chunk prefill for internal chunk c: Tb and scale * P rows.
+inline size_t chunk_workspace_bytes(int64_t total_tokens, int32_t heads, int c) {
+    return (size_t)2 * (size_t)total_tokens * (size_t)heads * (size_t)c * sizeof(float);
+}
 
 struct DecodeArgs {
     const void *q, *k, *v;
@@ -45,10 +51,12 @@ struct DecodeArgs {
 // Each launcher returns hipSuccess, hipErrorNotSupported for a shape it has no
 // kernel for (checked before anything is enqueued), or the launch error.
 hipError_t launch_short_conv(const ConvArgs &a, bool bf16, hipStream_t s);
-// Chunk prefill per dtype: with launch == false only *ok (shape supported) is set.
-hipError_t launch_chunk_bf16_f32out(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok);
-hipError_t launch_chunk_bf16_bf16out(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok);
-hipError_t launch_chunk_f32(const ChunkArgs &a, hipStream_t s, bool launch, bool *ok);
+// Chunk prefill per dtype: *chunk_used receives the internal chunk size (0 if the
+// shape is not supported); with launch == false nothing is enqueued.
+hipError_t launch_chunk_bf16_f32out(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
+hipError_t launch_chunk_bf16_bf16out(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
+hipError_t launch_chunk_f32(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
+typedef hipError_t (*ChunkLauncher)(const ChunkArgs &, hipStream_t, bool, int *);
 hipError_t launch_decode_step(const DecodeArgs &a, bool bf16, hipStream_t s);
 
 }  // namespace kda

@@ -124,13 +124,24 @@ KDA_API kda_status_t kda_short_conv(const void *x, const void *weight, const voi
  *   final_state    [num_seqs, num_heads, dk, dv]   fp32, or NULL = not written;
  *                  may alias initial_state.
  *   o              [total_tokens, num_heads, dv]   out_dtype; must not alias any input.
+ *   workspace      device scratch of at least kda_chunk_fwd_workspace_size() bytes,
+ *                  16-byte aligned, owned by the caller, not aliasing any argument;
+ *                  its contents on entry do not matter and are undefined on exit
+ *                  (NULL is allowed with zero tokens).  It holds, for every token
+ *                  and head, the token's row of Tb = (I + diag(beta) A)^{-1} diag(beta)
+ *                  and of scale * P within its chunk (see below); calls that share
+ *                  a workspace must be ordered on one stream.
  * scale is the read-out scale (the pages leave the query scale to the caller;
  * dk^-1/2 is the usual choice).  gate_lower_bound is the floor of g promised by
  * the caller ([Walkthrough] 彩蛋: the bounded gate keeps sub-chunk decay products
  * inside the floating-point range); it must be in [-9, 0].  g below the
  * promised floor gives unspecified accuracy but no out-of-bounds access.
  * Supported: dk, dv in {16, 32, 64, 128}; chunk_size in {16, 32, 64};
- * |q|, |k| entries below 1e3.  The fp32 dtype computes in fp32 throughout; the
+ * |q|, |k| entries below 1e3.  Two kernels run on `stream`: the first computes,
+ * for every chunk and head at once, the chunk's Tb and the decayed, scaled
+ * in-chunk products scale * P_ti = scale * sum_c q_tc k_ic e^{G_tc - G_ic} (i <= t,
+ * G the in-chunk cumulative g), which depend on q, k, g, beta only; the second
+ * walks the chunks of every sequence with the state on chip.  The fp32 dtype computes in fp32 throughout; the
  * bf16 dtype runs its products on bf16 matrix cores with fp32 accumulation,
  * keeps the recurrent state in fp32 and gives every product split operands
  * (x = hi + lo, both bf16; three-term products), which keeps the products near
@@ -143,7 +154,19 @@ KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, 
                            int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
                            int32_t chunk_size, float scale, float gate_lower_bound,
                            const float *initial_state, float *final_state, void *o,
-                           kda_dtype_t dtype, kda_dtype_t out_dtype, void *stream);
+                           void *workspace, size_t workspace_bytes, kda_dtype_t dtype,
+                           kda_dtype_t out_dtype, void *stream);
+
+/*
+ * kda_chunk_fwd_workspace_size -- bytes of device workspace kda_chunk_fwd needs
+ * for these sizes (written to *bytes): 2 * total_tokens * num_heads * C * 4,
+ * where C is the internal chunk size chosen for (dtype, dk, dv, chunk_size).
+ * Returns the same status kda_chunk_fwd would return for an unsupported shape.
+ */
+KDA_API kda_status_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_heads,
+                                                  int32_t dk, int32_t dv, int32_t chunk_size,
+                                                  kda_dtype_t dtype, kda_dtype_t out_dtype,
+                                                  size_t *bytes);
 
 /*
  * kda_decode_step -- one recurrent KDA step for a batch of sequences, updating

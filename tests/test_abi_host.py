@@ -32,8 +32,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"kda_short_conv", "kda_chunk_fwd", "kda_decode_step",
-                          "kda_status_string", "kda_last_error", "kda_version"}
+    assert set(names) == {"kda_short_conv", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
+                          "kda_decode_step", "kda_status_string", "kda_last_error",
+                          "kda_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -55,11 +56,32 @@ def test_status_strings_and_version(lib):
 
 def chunk(lib, **kw):
     a = dict(q=P, k=P, v=P, g=P, beta=P, cu=NULL, N=1, T=64, H=2, dk=128, dv=128, chunk=64,
-             scale=0.1, lb=-5.0, h0=NULL, hT=NULL, o=ctypes.c_void_p(8192), dtype=BF16, odt=F32)
+             scale=0.1, lb=-5.0, h0=NULL, hT=NULL, o=ctypes.c_void_p(8192),
+             ws=ctypes.c_void_p(1 << 20), wsb=1 << 30, dtype=BF16, odt=F32)
     a.update(kw)
     return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"], a["T"],
                              a["H"], a["dk"], a["dv"], a["chunk"], a["scale"], a["lb"], a["h0"],
-                             a["hT"], a["o"], a["dtype"], a["odt"], NULL)
+                             a["hT"], a["o"], a["ws"], a["wsb"], a["dtype"], a["odt"], NULL)
+
+
+def ws_size(lib, T=64, H=2, dk=128, dv=128, chunk=64, dtype=BF16, odt=F32):
+    n = ctypes.c_size_t(0)
+    st = lib.kda_chunk_fwd_workspace_size(T, H, dk, dv, chunk, dtype, odt, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size(lib):
+    # two fp32 rows of the internal chunk (32 or 16 tokens) per token and head
+    assert ws_size(lib) == (kda.KDA_OK, 2 * 64 * 2 * 32 * 4)
+    assert ws_size(lib, chunk=16) == (kda.KDA_OK, 2 * 64 * 2 * 16 * 4)
+    assert ws_size(lib, T=0) == (kda.KDA_OK, 0)
+    assert ws_size(lib, dtype=F32, dk=16, dv=16, chunk=32) == (kda.KDA_OK, 2 * 64 * 2 * 32 * 4)
+    assert ws_size(lib, dk=48)[0] == kda.KDA_ERR_UNSUPPORTED
+    assert ws_size(lib, chunk=8)[0] == kda.KDA_ERR_UNSUPPORTED
+    assert ws_size(lib, dtype=F32, odt=BF16)[0] == kda.KDA_ERR_UNSUPPORTED
+    assert ws_size(lib, H=0)[0] == kda.KDA_ERR_INVALID_ARG
+    assert lib.kda_chunk_fwd_workspace_size(64, 2, 128, 128, 64, BF16, F32, None) == \
+        kda.KDA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -81,6 +103,9 @@ def chunk(lib, **kw):
     (dict(dv=256), kda.KDA_ERR_UNSUPPORTED),
     (dict(chunk=128), kda.KDA_ERR_UNSUPPORTED),
     (dict(chunk=8), kda.KDA_ERR_UNSUPPORTED),
+    (dict(ws=NULL), kda.KDA_ERR_INVALID_ARG),
+    (dict(wsb=2 * 64 * 2 * 32 * 4 - 1), kda.KDA_ERR_INVALID_ARG),   # one byte short
+    (dict(o=ctypes.c_void_p(1 << 20)), kda.KDA_ERR_INVALID_ARG),     # o aliases the workspace
 ])
 def test_chunk_fwd_rejects(lib, kw, status):
     assert chunk(lib, **kw) == status
