@@ -51,17 +51,29 @@ __device__ __forceinline__ void split2(float x, bf16 &hh, bf16 &ll) {
     ll = (bf16)(x - (float)hh);
 }
 
+// Split two floats into packed bf16 pairs hi = (h0, h1), lo = (l0, l1) with
+// x = h + l: one packed conversion for the high parts, their exact fp32 values
+// by shifting the bits back, two subtractions, one packed conversion.
+__device__ __forceinline__ void split_pair(float x0, float x1, bf16x2 &hi, bf16x2 &lo) {
+    bf16x2 h;
+    h[0] = (bf16)x0;
+    h[1] = (bf16)x1;
+    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+    const float h0 = __uint_as_float(hb << 16), h1 = __uint_as_float(hb & 0xffff0000u);
+    bf16x2 l;
+    l[0] = (bf16)(x0 - h0);
+    l[1] = (bf16)(x1 - h1);
+    hi = h;
+    lo = l;
+}
+
 // Store x0, x1 at H[i], H[i+1] (and the low parts at L[i], L[i+1] when T is bf16).
 template <class T>
 __device__ __forceinline__ void put2(T *H, T *L, int i, float x0, float x1) {
     typedef typename Pair<T>::type P2;
     if constexpr (std::is_same<T, bf16>::value) {
-        bf16 h0, l0, h1, l1;
-        split2(x0, h0, l0);
-        split2(x1, h1, l1);
         P2 h, l;
-        h[0] = h0; h[1] = h1;
-        l[0] = l0; l[1] = l1;
+        split_pair(x0, x1, h, l);
         *reinterpret_cast<P2 *>(H + i) = h;
         *reinterpret_cast<P2 *>(L + i) = l;
     } else {
@@ -115,23 +127,31 @@ __device__ __forceinline__ void rescale_split(F &hi, F &lo, const float *s) {
 struct BReg8 { bf16x8 h, l; };
 struct BReg4 { bf16x4 h, l; };
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t bits(bf16x2 x) { return __builtin_bit_cast(uint32_t, x); }
+
+// Split accumulator tiles into (hi, lo) B operands, assembling the vectors from
+// whole 32-bit pairs (no per-element insertion).
 __device__ __forceinline__ BReg8 breg8(const f32x4 &a, const f32x4 &b) {
+    bf16x2 h0, l0, h1, l1, h2, l2, h3, l3;
+    split_pair(a[0], a[1], h0, l0);
+    split_pair(a[2], a[3], h1, l1);
+    split_pair(b[0], b[1], h2, l2);
+    split_pair(b[2], b[3], h3, l3);
     BReg8 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        bf16 hh, ll;
-        split2(a[e], hh, ll); r.h[e] = hh; r.l[e] = ll;
-        split2(b[e], hh, ll); r.h[e + 4] = hh; r.l[e + 4] = ll;
-    }
+    r.h = __builtin_bit_cast(bf16x8, u32x4{bits(h0), bits(h1), bits(h2), bits(h3)});
+    r.l = __builtin_bit_cast(bf16x8, u32x4{bits(l0), bits(l1), bits(l2), bits(l3)});
     return r;
 }
 __device__ __forceinline__ BReg4 breg4(const f32x4 &a) {
+    bf16x2 h0, l0, h1, l1;
+    split_pair(a[0], a[1], h0, l0);
+    split_pair(a[2], a[3], h1, l1);
     BReg4 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        bf16 hh, ll;
-        split2(a[e], hh, ll); r.h[e] = hh; r.l[e] = ll;
-    }
+    r.h = __builtin_bit_cast(bf16x4, u32x2{bits(h0), bits(h1)});
+    r.l = __builtin_bit_cast(bf16x4, u32x2{bits(l0), bits(l1)});
     return r;
 }
 
@@ -139,15 +159,12 @@ __device__ __forceinline__ BReg4 breg4(const f32x4 &a) {
 __device__ __forceinline__ void afrag8(const bf16 *Mh, const bf16 *Ml, int ld, int row0, int k0,
                                        int lane, bf16x8 &hh, bf16x8 &ll) {
     const int off = (row0 + (lane & 15)) * ld + k0 + (lane >> 4) * 4;
-    const bf16x4 h0 = *reinterpret_cast<const bf16x4 *>(Mh + off);
-    const bf16x4 h1 = *reinterpret_cast<const bf16x4 *>(Mh + off + 16);
-    const bf16x4 l0 = *reinterpret_cast<const bf16x4 *>(Ml + off);
-    const bf16x4 l1 = *reinterpret_cast<const bf16x4 *>(Ml + off + 16);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        hh[e] = h0[e]; hh[e + 4] = h1[e];
-        ll[e] = l0[e]; ll[e + 4] = l1[e];
-    }
+    const u32x2 h0 = *reinterpret_cast<const u32x2 *>(Mh + off);
+    const u32x2 h1 = *reinterpret_cast<const u32x2 *>(Mh + off + 16);
+    const u32x2 l0 = *reinterpret_cast<const u32x2 *>(Ml + off);
+    const u32x2 l1 = *reinterpret_cast<const u32x2 *>(Ml + off + 16);
+    hh = __builtin_bit_cast(bf16x8, u32x4{h0[0], h0[1], h1[0], h1[1]});
+    ll = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
 }
 __device__ __forceinline__ void afrag4(const bf16 *Mh, const bf16 *Ml, int ld, int row0, int k0,
                                        int lane, bf16x4 &hh, bf16x4 &ll) {

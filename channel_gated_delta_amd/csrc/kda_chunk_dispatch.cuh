@@ -30,7 +30,7 @@ inline int pick_bv(int dv) {
 // Internal chunk: the largest of 64, 32, 16 that is not above the requested size
 // nor the preferred maximum (KDA_CHUNK_MAX) and whose working sets fit in LDS.
 #ifndef KDA_CHUNK_MAX
-#define KDA_CHUNK_MAX 32
+#define KDA_CHUNK_MAX 16
 #endif
 template <class T, int DK>
 int pick_chunk(int chunk) {

@@ -62,6 +62,169 @@ struct StateCfg {
     static constexpr bool kFits = kLds <= 160 * 1024;
 };
 
+// A fragments (hi, lo) in the permuted k order of the register-B products.
+struct AF8 { bf16x8 h, l; };
+struct AF4 { bf16x4 h, l; };
+
+__device__ __forceinline__ AF8 lda8(const bf16 *Mh, const bf16 *Ml, int ld, int row0, int k0,
+                                    int lane) {
+    AF8 f;
+    afrag8(Mh, Ml, ld, row0, k0, lane, f.h, f.l);
+    return f;
+}
+__device__ __forceinline__ AF4 lda4(const bf16 *Mh, const bf16 *Ml, int ld, int row0, int k0,
+                                    int lane) {
+    AF4 f;
+    afrag4(Mh, Ml, ld, row0, k0, lane, f.h, f.l);
+    return f;
+}
+__device__ __forceinline__ BReg4 low_half(const BReg8 &b) {
+    const u32x4 h = __builtin_bit_cast(u32x4, b.h), l = __builtin_bit_cast(u32x4, b.l);
+    BReg4 r;
+    r.h = __builtin_bit_cast(bf16x4, u32x2{h[0], h[1]});
+    r.l = __builtin_bit_cast(bf16x4, u32x2{l[0], l[1]});
+    return r;
+}
+
+// The state chain of one chunk for one consumer wave, bf16 operands, dk a
+// multiple of 32 and chunks of 16 or 32 tokens.  Written as explicit stages
+// whose LDS fragment loads are issued one stage ahead of the products that use
+// them (scheduling barriers keep the compiler from sinking the loads next to
+// their first use, which would expose the LDS latency at every product).
+template <int DK, int C, int LDK, int LDC, int LDV>
+__device__ __forceinline__ void state_chain_bf16(
+    f32x4 (&Sacc)[DK / 16], f32x4 (&Ot)[C / 16], const bf16 *sQdh, const bf16 *sQdl,
+    const bf16 *sKdh, const bf16 *sKdl, const bf16 *sKrTh, const bf16 *sKrTl, const bf16 *sTbh,
+    const bf16 *sTbl, const bf16 *sPh, const bf16 *sPl, const float *sV, const float *sEGn,
+    int wcol, int lane) {
+    constexpr int NTK = DK / 16, NKB = DK / 32, NTC = C / 16;
+    static_assert(DK % 32 == 0 && (C == 16 || C == 32), "shape");
+    // small operands first: Tb / P fragments and V
+    const AF4 tb0 = lda4(sTbh, sTbl, LDC, 0, 0, lane), p0 = lda4(sPh, sPl, LDC, 0, 0, lane);
+    AF8 tb1, p1;
+    if constexpr (NTC == 2) {
+        tb1 = lda8(sTbh, sTbl, LDC, 16, 0, lane);
+        p1 = lda8(sPh, sPl, LDC, 16, 0, lane);
+    }
+    float vin[NTC][4];
+#pragma unroll
+    for (int R = 0; R < NTC; ++R)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vin[R][r] = sV[(R * 16 + acc_row(lane, r)) * LDV + wcol + (lane & 15)];
+    AF8 fk[2][NTC], fq[2][NTC];
+#pragma unroll
+    for (int R = 0; R < NTC; ++R) {
+        fk[0][R] = lda8(sKdh, sKdl, LDK, R * 16, 0, lane);
+        fq[0][R] = lda8(sQdh, sQdl, LDK, R * 16, 0, lane);
+    }
+    // the state as B operand (hi, lo)
+    BReg8 sb[NKB];
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) sb[j] = breg8(Sacc[2 * j], Sacc[2 * j + 1]);
+
+    // E = Kd S, O = Qd S: k-block j's products while block j+1 loads
+    f32x4 Et[NTC];
+#pragma unroll
+    for (int R = 0; R < NTC; ++R) {
+        Et[R] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Ot[R] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+        const int cur = j & 1, nxt = cur ^ 1;
+        if (j + 1 < NKB) {
+#pragma unroll
+            for (int R = 0; R < NTC; ++R) {
+                fk[nxt][R] = lda8(sKdh, sKdl, LDK, R * 16, 32 * (j + 1), lane);
+                fq[nxt][R] = lda8(sQdh, sQdl, LDK, R * 16, 32 * (j + 1), lane);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // term-major order: the 2*NTC accumulators interleave, so no product waits
+        // for the one before it
+#pragma unroll
+        for (int R = 0; R < NTC; ++R) {
+            Et[R] = mma(fk[cur][R].h, sb[j].h, Et[R]);
+            Ot[R] = mma(fq[cur][R].h, sb[j].h, Ot[R]);
+        }
+#pragma unroll
+        for (int R = 0; R < NTC; ++R) {
+            Et[R] = mma(fk[cur][R].h, sb[j].l, Et[R]);
+            Ot[R] = mma(fq[cur][R].h, sb[j].l, Ot[R]);
+        }
+#pragma unroll
+        for (int R = 0; R < NTC; ++R) {
+            Et[R] = mma(fk[cur][R].l, sb[j].h, Et[R]);
+            Ot[R] = mma(fq[cur][R].l, sb[j].h, Ot[R]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // first half of the state-update fragments load during the U and P U products
+    constexpr int NK1 = NTK / 2;
+    AF8 fr8[NTK];
+    AF4 fr4[NTK];
+#pragma unroll
+    for (int rt = 0; rt < NK1; ++rt) {
+        if constexpr (C == 32) fr8[rt] = lda8(sKrTh, sKrTl, LDC, rt * 16, 0, lane);
+        else fr4[rt] = lda4(sKrTh, sKrTl, LDC, rt * 16, 0, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // E = V - Kd S;  U = Tb E
+#pragma unroll
+    for (int R = 0; R < NTC; ++R)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Et[R][r] = vin[R][r] - Et[R][r];
+    f32x4 Ut[NTC];
+    BReg8 ub8;
+    BReg4 ub4;
+    if constexpr (NTC == 2) {
+        const BReg8 eb = breg8(Et[0], Et[1]);
+        Ut[0] = mma3(tb0.h, tb0.l, low_half(eb), f32x4{0.f, 0.f, 0.f, 0.f});
+        Ut[1] = mma3(tb1.h, tb1.l, eb, f32x4{0.f, 0.f, 0.f, 0.f});
+        ub8 = breg8(Ut[0], Ut[1]);
+        ub4 = low_half(ub8);
+        Ot[0] = mma3(p0.h, p0.l, ub4, Ot[0]);
+        Ot[1] = mma3(p1.h, p1.l, ub8, Ot[1]);
+    } else {
+        const BReg4 eb = breg4(Et[0]);
+        Ut[0] = mma3(tb0.h, tb0.l, eb, f32x4{0.f, 0.f, 0.f, 0.f});
+        ub4 = breg4(Ut[0]);
+        Ot[0] = mma3(p0.h, p0.l, ub4, Ot[0]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // second half of the fragments load during the first half's products
+#pragma unroll
+    for (int rt = NK1; rt < NTK; ++rt) {
+        if constexpr (C == 32) fr8[rt] = lda8(sKrTh, sKrTl, LDC, rt * 16, 0, lane);
+        else fr4[rt] = lda4(sKrTh, sKrTl, LDC, rt * 16, 0, lane);
+    }
+    f32x4 eg[NTK];
+#pragma unroll
+    for (int rt = 0; rt < NTK; ++rt)
+        eg[rt] = *reinterpret_cast<const f32x4 *>(sEGn + rt * 16 + (lane >> 4) * 4);
+    __builtin_amdgcn_sched_barrier(0);
+    // S = diag(e^{G_n}) S + Kr^T U (term-major over the NTK accumulators)
+#pragma unroll
+    for (int rt = 0; rt < NTK; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Sacc[rt][r] *= eg[rt][r];
+    if constexpr (C == 32) {
+#pragma unroll
+        for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr8[rt].h, ub8.h, Sacc[rt]);
+#pragma unroll
+        for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr8[rt].h, ub8.l, Sacc[rt]);
+#pragma unroll
+        for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr8[rt].l, ub8.h, Sacc[rt]);
+    } else {
+#pragma unroll
+        for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr4[rt].h, ub4.h, Sacc[rt]);
+#pragma unroll
+        for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr4[rt].h, ub4.l, Sacc[rt]);
+#pragma unroll
+        for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr4[rt].l, ub4.h, Sacc[rt]);
+    }
+}
+
 template <class T, class TO, int DK, int BV, int C>
 __global__ __launch_bounds__(512, 1)
 void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
@@ -94,6 +257,7 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
     const int64_t bos = chunk_seq_off(cu_seqlens, n, total);
     const int64_t eos = max(chunk_seq_off(cu_seqlens, n + 1, total), bos);
     const int nchunks = (int)((eos - bos + C - 1) / C);
+    const int nsteps = (nchunks + 2) & ~1;   // steps 1..nchunks consume chunks 0..nchunks-1
     const int v0 = slice * BV;
     const size_t rowQK = (size_t)H * DK, rowV = (size_t)H * DV;
 
@@ -107,143 +271,177 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
         const int tr = (pt * NTB) / C, tc = (pt * NTB) % C;   // Tb / P: row tr, cols tc..
         const int vr = (pt * NVE) / BV, vcol = (pt * NVE) % BV;  // V: row vr, cols vcol..
 
-        T2 pq[RP], pk[RP];
-        f32x2 pg[RP];
-        float ptb[NTB], ppm[NTB];
-        TV pvv;
-        auto issue_loads = [&](int64_t cs) {
+        // Two register sets for the prefetched inputs, used alternately: the loads
+        // for chunk s+1 never target registers still holding chunk s, so no copy
+        // (and no wait for the loads) is needed between steps.
+        constexpr int NTB4 = NTB >= 4 ? NTB / 4 : 1;
+        struct Regs {
+            T2 q[RP], k[RP];
+            f32x2 g[RP];
+            f32x4 tb[NTB4], pm[NTB4];   // NTB == 1 uses element 0 of the first vector
+            TV v;
+        };
+        // Chunk bases are uniform 64-bit pointers; per-lane offsets inside a chunk
+        // fit 32 bits (rows < C), which keeps the address arithmetic scalar.
+        auto load = [&](Regs &R, int64_t cs) {
             const int last = (int)min((int64_t)C, eos - cs) - 1;
+            const size_t bq = (size_t)cs * rowQK + (size_t)h * DK;
+            const T *qb = q + bq, *kb = k + bq;
+            const float *gb = g + bq;
             if (act) {
 #pragma unroll
                 for (int j = 0; j < RP; ++j) {
-                    const size_t off = (size_t)(cs + min(rg * RP + j, last)) * rowQK +
-                                       (size_t)h * DK + 2 * cpair;
-                    pq[j] = *reinterpret_cast<const T2 *>(q + off);
-                    pk[j] = *reinterpret_cast<const T2 *>(k + off);
-                    pg[j] = *reinterpret_cast<const f32x2 *>(g + off);
+                    const uint32_t off = (uint32_t)min(rg * RP + j, last) * (uint32_t)rowQK +
+                                         (uint32_t)(2 * cpair);
+                    R.q[j] = *reinterpret_cast<const T2 *>(qb + off);
+                    R.k[j] = *reinterpret_cast<const T2 *>(kb + off);
+                    R.g[j] = *reinterpret_cast<const f32x2 *>(gb + off);
                 }
             }
-            const size_t wo = ((size_t)(cs + min(tr, last)) * H + h) * C + tc;
+            const float *tbb = tb + ((size_t)cs * H + h) * C, *pmb = pm + ((size_t)cs * H + h) * C;
+            const uint32_t wo = (uint32_t)min(tr, last) * (uint32_t)(H * C) + (uint32_t)tc;
             if constexpr (NTB == 1) {
-                ptb[0] = tb[wo];
-                ppm[0] = pm[wo];
+                R.tb[0][0] = tbb[wo];
+                R.pm[0][0] = pmb[wo];
             } else {
 #pragma unroll
-                for (int j = 0; j < NTB / 4; ++j) {
-                    const f32x4 a = *reinterpret_cast<const f32x4 *>(tb + wo + 4 * j);
-                    const f32x4 c = *reinterpret_cast<const f32x4 *>(pm + wo + 4 * j);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        ptb[4 * j + e] = a[e];
-                        ppm[4 * j + e] = c[e];
-                    }
+                for (int j = 0; j < NTB4; ++j) {
+                    R.tb[j] = *reinterpret_cast<const f32x4 *>(tbb + wo + 4 * j);
+                    R.pm[j] = *reinterpret_cast<const f32x4 *>(pmb + wo + 4 * j);
                 }
             }
-            pvv = *reinterpret_cast<const TV *>(v + (size_t)(cs + min(vr, last)) * rowV +
-                                                (size_t)h * DV + v0 + vcol);
+            const T *vb = v + (size_t)cs * rowV + (size_t)h * DV + v0;
+            R.v = *reinterpret_cast<const TV *>(vb + (uint32_t)min(vr, last) * (uint32_t)rowV +
+                                                (uint32_t)vcol);
         };
-        if (nchunks > 0) issue_loads(bos);
 
-        for (int s = 0; s <= nchunks; ++s) {
-            if (s < nchunks) {
-                const int64_t cs = bos + (int64_t)s * C;
-                const int nt = (int)min((int64_t)C, eos - cs);
-                char *st = smem + (s & 1) * Cfg::kStage;
-                T *sQdh = reinterpret_cast<T *>(st + Cfg::oQd), *sQdl = sQdh + (SPLIT ? CKE : 0);
-                T *sKdh = reinterpret_cast<T *>(st + Cfg::oKd), *sKdl = sKdh + (SPLIT ? CKE : 0);
-                T *sKrTh = reinterpret_cast<T *>(st + Cfg::oKrT), *sKrTl = sKrTh + (SPLIT ? KCE : 0);
-                T *sTbh = reinterpret_cast<T *>(st + Cfg::oTb), *sTbl = sTbh + (SPLIT ? CCE : 0);
-                T *sPh = reinterpret_cast<T *>(st + Cfg::oP), *sPl = sPh + (SPLIT ? CCE : 0);
-                float *sV = reinterpret_cast<float *>(st + Cfg::oV);
-                float *sEGn = reinterpret_cast<float *>(st + Cfg::oEGn);
+        // Step s: build stage s & 1 from chunk s (if s < nchunks) out of `cur`, and
+        // load chunk s+1 (clamped to the last chunk) into `nxt`.
+        auto step = [&](Regs &cur, Regs &nxt, int s) {
+            const bool work = s < nchunks;
+            const int64_t cs = bos + (int64_t)s * C;
+            const int nt = work ? (int)min((int64_t)C, eos - cs) : 0;
+            // Rows past the end of the sequence (nt <= row < C) hold a copy of the last
+            // row.  Only g (so the decay stops there) and the Tb, P rows are zeroed:
+            // zero rows of Tb make U zero there, which removes every other
+            // contribution of those rows (V, k e^G, k e^{Gn-G}); their rows of
+            // scale q e^G only produce outputs that are never stored.
+            float qv[RP][2], kv[RP][2], gam[RP][2];
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int j = 0; j < RP; ++j) {
+                const bool in = rg * RP + j < nt;
+                qv[j][0] = to_f32(cur.q[j][0]);
+                qv[j][1] = to_f32(cur.q[j][1]);
+                kv[j][0] = to_f32(cur.k[j][0]);
+                kv[j][1] = to_f32(cur.k[j][1]);
+                a0 += (in ? cur.g[j][0] : 0.f) * kLog2e;
+                a1 += (in ? cur.g[j][1] : 0.f) * kLog2e;
+                gam[j][0] = a0;
+                gam[j][1] = a1;
+            }
+            float tbv[NTB], pmv[NTB];
+#pragma unroll
+            for (int e = 0; e < NTB; ++e) {
+                tbv[e] = tr < nt ? cur.tb[e / 4][e % 4] : 0.f;
+                pmv[e] = tr < nt ? cur.pm[e / 4][e % 4] : 0.f;
+            }
+            float vv[NVE];
+#pragma unroll
+            for (int e = 0; e < NVE; ++e) vv[e] = to_f32(cur.v[e]);
+            // `cur` was loaded a step ago: wait for it explicitly before the next loads
+            // are issued (vmcnt(0) here costs nothing).  Global loads and stores share
+            // one in-order counter, so a wait placed after the new loads -- where the
+            // compiler would put it, at the first use of `cur` -- also waits for them.
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt untouched
+            if (nchunks > 0) load(nxt, bos + (int64_t)min(s + 1, nchunks - 1) * C);
+            // Pin the loads here: the step barriers order LDS only, so without a
+            // compiler memory barrier the loads would be sunk to their use in the
+            // next step and their latency exposed there.
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            if (!work) return;
 
-                // consume the registers (rows >= nt are zero)
-                float qv[RP][2], kv[RP][2], gam[RP][2];
-                float a0 = 0.f, a1 = 0.f;
+            char *st = smem + (s & 1) * Cfg::kStage;
+            T *sQdh = reinterpret_cast<T *>(st + Cfg::oQd), *sQdl = sQdh + (SPLIT ? CKE : 0);
+            T *sKdh = reinterpret_cast<T *>(st + Cfg::oKd), *sKdl = sKdh + (SPLIT ? CKE : 0);
+            T *sKrTh = reinterpret_cast<T *>(st + Cfg::oKrT), *sKrTl = sKrTh + (SPLIT ? KCE : 0);
+            T *sTbh = reinterpret_cast<T *>(st + Cfg::oTb), *sTbl = sTbh + (SPLIT ? CCE : 0);
+            T *sPh = reinterpret_cast<T *>(st + Cfg::oP), *sPl = sPh + (SPLIT ? CCE : 0);
+            float *sV = reinterpret_cast<float *>(st + Cfg::oV);
+            float *sEGn = reinterpret_cast<float *>(st + Cfg::oEGn);
+            {
+                const int i = tr * LDC + tc;
+                if constexpr (NTB == 1) {
+                    put1(sTbh, sTbl, i, tbv[0]);
+                    put1(sPh, sPl, i, pmv[0]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < NTB; e += 2) {
+                        put2(sTbh, sTbl, i + e, tbv[e], tbv[e + 1]);
+                        put2(sPh, sPl, i + e, pmv[e], pmv[e + 1]);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < NVE; ++e) sV[vr * LDV + vcol + e] = vv[e];
+            }
+
+            // prefix of the row-group sums (lanes rg*CPW + i share a channel pair)
+            float inc0 = a0, inc1 = a1;
+#pragma unroll
+            for (int d = 1; d < RG; d <<= 1) {
+                const float u0 = __shfl_up(inc0, d * CPW, kWave);
+                const float u1 = __shfl_up(inc1, d * CPW, kWave);
+                if (rg >= d) {
+                    inc0 += u0;
+                    inc1 += u1;
+                }
+            }
+            const int lastl = (RG - 1) * CPW + (lane % CPW);
+            const float tot0 = __shfl(inc0, lastl, kWave), tot1 = __shfl(inc1, lastl, kWave);
+            const float off0 = inc0 - a0, off1 = inc1 - a1;
+
+            if (act) {
+                float krt[2][RP];
 #pragma unroll
                 for (int j = 0; j < RP; ++j) {
-                    const bool in = act && rg * RP + j < nt;
-                    qv[j][0] = in ? to_f32(pq[j][0]) : 0.f;
-                    qv[j][1] = in ? to_f32(pq[j][1]) : 0.f;
-                    kv[j][0] = in ? to_f32(pk[j][0]) : 0.f;
-                    kv[j][1] = in ? to_f32(pk[j][1]) : 0.f;
-                    a0 += (in ? pg[j][0] : 0.f) * kLog2e;
-                    a1 += (in ? pg[j][1] : 0.f) * kLog2e;
-                    gam[j][0] = a0;
-                    gam[j][1] = a1;
+                    const float g0 = gam[j][0] + off0, g1 = gam[j][1] + off1;
+                    // all exponents are <= 0 for g <= 0 (the gate's contract)
+                    const float e0 = exp2_nonpos(g0), e1 = exp2_nonpos(g1);
+                    krt[0][j] = kv[j][0] * exp2_nonpos(tot0 - g0);
+                    krt[1][j] = kv[j][1] * exp2_nonpos(tot1 - g1);
+                    const int i = (rg * RP + j) * LDK + 2 * cpair;
+                    put2(sQdh, sQdl, i, qv[j][0] * e0 * scale, qv[j][1] * e1 * scale);
+                    put2(sKdh, sKdl, i, kv[j][0] * e0, kv[j][1] * e1);
                 }
-                float tbv[NTB], pmv[NTB];
 #pragma unroll
-                for (int e = 0; e < NTB; ++e) {
-                    tbv[e] = tr < nt ? ptb[e] : 0.f;
-                    pmv[e] = tr < nt ? ppm[e] : 0.f;
-                }
-                float vv[NVE];
+                for (int e = 0; e < 2; ++e) {
+                    const int base = (2 * cpair + e) * LDC + rg * RP;
+                    if constexpr (RP % 2 == 0) {
 #pragma unroll
-                for (int e = 0; e < NVE; ++e) vv[e] = vr < nt ? to_f32(pvv[e]) : 0.f;
-                if (s + 1 < nchunks) issue_loads(cs + C);
-
-                // prefix of the row-group sums (lanes rg*CPW + i share a channel pair)
-                float inc0 = a0, inc1 = a1;
-#pragma unroll
-                for (int d = 1; d < RG; d <<= 1) {
-                    const float u0 = __shfl_up(inc0, d * CPW, kWave);
-                    const float u1 = __shfl_up(inc1, d * CPW, kWave);
-                    if (rg >= d) {
-                        inc0 += u0;
-                        inc1 += u1;
-                    }
-                }
-                const int lastl = (RG - 1) * CPW + (lane % CPW);
-                const float tot0 = __shfl(inc0, lastl, kWave), tot1 = __shfl(inc1, lastl, kWave);
-                const float off0 = inc0 - a0, off1 = inc1 - a1;
-
-                if (act) {
-                    float krt[2][RP];
-#pragma unroll
-                    for (int j = 0; j < RP; ++j) {
-                        const float g0 = gam[j][0] + off0, g1 = gam[j][1] + off1;
-                        const float e0 = exp2_clamped(g0), e1 = exp2_clamped(g1);
-                        krt[0][j] = kv[j][0] * exp2_clamped(tot0 - g0);
-                        krt[1][j] = kv[j][1] * exp2_clamped(tot1 - g1);
-                        const int i = (rg * RP + j) * LDK + 2 * cpair;
-                        put2(sQdh, sQdl, i, qv[j][0] * e0 * scale, qv[j][1] * e1 * scale);
-                        put2(sKdh, sKdl, i, kv[j][0] * e0, kv[j][1] * e1);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const int base = (2 * cpair + e) * LDC + rg * RP;
-                        if constexpr (RP % 2 == 0) {
-#pragma unroll
-                            for (int j = 0; j < RP; j += 2)
-                                put2(sKrTh, sKrTl, base + j, krt[e][j], krt[e][j + 1]);
-                        } else {
-#pragma unroll
-                            for (int j = 0; j < RP; ++j) put1(sKrTh, sKrTl, base + j, krt[e][j]);
-                        }
-                    }
-                    if (rg == 0) {
-                        sEGn[2 * cpair] = exp2_clamped(tot0);
-                        sEGn[2 * cpair + 1] = exp2_clamped(tot1);
-                    }
-                }
-                {
-                    const int i = tr * LDC + tc;
-                    if constexpr (NTB == 1) {
-                        put1(sTbh, sTbl, i, tbv[0]);
-                        put1(sPh, sPl, i, pmv[0]);
+                        for (int j = 0; j < RP; j += 2)
+                            put2(sKrTh, sKrTl, base + j, krt[e][j], krt[e][j + 1]);
                     } else {
 #pragma unroll
-                        for (int e = 0; e < NTB; e += 2) {
-                            put2(sTbh, sTbl, i + e, tbv[e], tbv[e + 1]);
-                            put2(sPh, sPl, i + e, pmv[e], pmv[e + 1]);
-                        }
+                        for (int j = 0; j < RP; ++j) put1(sKrTh, sKrTl, base + j, krt[e][j]);
                     }
-#pragma unroll
-                    for (int e = 0; e < NVE; ++e) sV[vr * LDV + vcol + e] = vv[e];
+                }
+                if (rg == 0) {
+                    sEGn[2 * cpair] = exp2_nonpos(tot0);
+                    sEGn[2 * cpair + 1] = exp2_nonpos(tot1);
                 }
             }
-            __syncthreads();
+        };
+
+        Regs A, B;
+        if (nchunks > 0) load(A, bos);
+        // nsteps = nchunks + 1 rounded up to even; one barrier per step
+        for (int s = 0; s < nsteps; s += 2) {
+            step(A, B, s);
+            lds_barrier();
+            step(B, A, s + 1);
+            lds_barrier();
         }
     } else {
         // =============================== consumers ===============================
@@ -260,8 +458,8 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                     Sacc[rt][r] = src[(size_t)(rt * 16 + acc_row(lane, r)) * DV + vc];
             }
         }
-        for (int s = 0; s <= nchunks; ++s) {
-            if (s >= 1 && owner) {
+        for (int s = 0; s < nsteps; ++s) {
+            if (s >= 1 && s <= nchunks && owner) {
                 const int64_t c0 = bos + (int64_t)(s - 1) * C;
                 const int nt = (int)min((int64_t)C, eos - c0);
                 const char *st = smem + ((s - 1) & 1) * Cfg::kStage;
@@ -278,6 +476,21 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                 const float *sV = reinterpret_cast<const float *>(st + Cfg::oV);
                 const float *sEGn = reinterpret_cast<const float *>(st + Cfg::oEGn);
 
+                if constexpr (SPLIT && DK % 32 == 0 && (C == 16 || C == 32)) {
+                    f32x4 Ot[NTC];
+                    state_chain_bf16<DK, C, LDK, LDC, LDV>(Sacc, Ot, sQdh, sQdl, sKdh, sKdl, sKrTh,
+                                                           sKrTl, sTbh, sTbl, sPh, sPl, sV, sEGn,
+                                                           wave * 16, lane);
+#pragma unroll
+                    for (int R = 0; R < NTC; ++R)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = R * 16 + acc_row(lane, r);
+                            if (row < nt)
+                                o[(size_t)(c0 + row) * rowV + (size_t)h * DV + vc] =
+                                    from_f32<TO>(Ot[R][r]);
+                        }
+                } else {
                 RegB<T, NTK> Sb;
                 Sb.prepare(Sacc);
                 f32x4 Et[NTC], Ot[NTC], Ut[NTC];
@@ -320,8 +533,9 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                     for (int r = 0; r < 4; ++r) Sacc[rt][r] *= sEGn[rt * 16 + acc_row(lane, r)];
                     Sacc[rt] = Ub.mul(Sacc[rt], sKrTh, sKrTl, LDC, rt * 16, NTC, lane);
                 }
+                }
             }
-            __syncthreads();
+            lds_barrier();
         }
         if (hT && owner) {
             float *dst = hT + ((size_t)unit * DK) * DV;

@@ -35,6 +35,19 @@ __device__ __forceinline__ float exp2_clamped(float x) {
     return __builtin_amdgcn_exp2f(fminf(x, 126.0f));
 }
 
+// 2^x for x <= 0 (the result is in [0, 1]; no clamp needed).
+__device__ __forceinline__ float exp2_nonpos(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup barrier that orders LDS accesses only.  Global loads and stores in
+// flight stay in flight: __syncthreads() would also wait for them, because one
+// counter tracks both global loads and stores, which defeats loads issued ahead
+// of their use.  Use only where no global-memory ordering between waves is needed.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {

@@ -71,11 +71,11 @@ def ws_size(lib, T=64, H=2, dk=128, dv=128, chunk=64, dtype=BF16, odt=F32):
 
 
 def test_workspace_size(lib):
-    # two fp32 rows of the internal chunk (32 or 16 tokens) per token and head
-    assert ws_size(lib) == (kda.KDA_OK, 2 * 64 * 2 * 32 * 4)
+    # two fp32 rows of the internal chunk (16 tokens unless built otherwise) per token and head
+    assert ws_size(lib) == (kda.KDA_OK, 2 * 64 * 2 * 16 * 4)
     assert ws_size(lib, chunk=16) == (kda.KDA_OK, 2 * 64 * 2 * 16 * 4)
     assert ws_size(lib, T=0) == (kda.KDA_OK, 0)
-    assert ws_size(lib, dtype=F32, dk=16, dv=16, chunk=32) == (kda.KDA_OK, 2 * 64 * 2 * 32 * 4)
+    assert ws_size(lib, dtype=F32, dk=16, dv=16, chunk=32) == (kda.KDA_OK, 2 * 64 * 2 * 16 * 4)
     assert ws_size(lib, dk=48)[0] == kda.KDA_ERR_UNSUPPORTED
     assert ws_size(lib, chunk=8)[0] == kda.KDA_ERR_UNSUPPORTED
     assert ws_size(lib, dtype=F32, odt=BF16)[0] == kda.KDA_ERR_UNSUPPORTED
@@ -104,7 +104,7 @@ def test_workspace_size(lib):
     (dict(chunk=128), kda.KDA_ERR_UNSUPPORTED),
     (dict(chunk=8), kda.KDA_ERR_UNSUPPORTED),
     (dict(ws=NULL), kda.KDA_ERR_INVALID_ARG),
-    (dict(wsb=2 * 64 * 2 * 32 * 4 - 1), kda.KDA_ERR_INVALID_ARG),   # one byte short
+    (dict(wsb=2 * 64 * 2 * 16 * 4 - 1), kda.KDA_ERR_INVALID_ARG),   # one byte short
     (dict(o=ctypes.c_void_p(1 << 20)), kda.KDA_ERR_INVALID_ARG),     # o aliases the workspace
 ])
 def test_chunk_fwd_rejects(lib, kw, status):
