@@ -27,7 +27,7 @@ kda_status_t from_hip(hipError_t e, const char *what) {
 
 bool valid_dtype(kda_dtype_t d) { return d == KDA_DTYPE_F32 || d == KDA_DTYPE_BF16; }
 bool head_dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
-int vec_elems(kda_dtype_t d) { return d == KDA_DTYPE_BF16 ? 8 : 4; }
+int vec_elems(kda_dtype_t) { return 4; }   // channels per lane of the conv kernel
 
 }  // namespace
 

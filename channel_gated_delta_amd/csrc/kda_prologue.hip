@@ -7,13 +7,14 @@
 // per channel.
 //
 // The prologue is a pure stream (read x once, write y once), so the kernel is
-// laid out for HBM: each lane owns one 16-byte vector of channels (8 bf16 or 4
-// fp32) and walks a tile of TT consecutive tokens, keeping the conv window in
-// registers; a wave covers 64 contiguous vectors of a token row, so every load
-// and store is a full 1 KiB coalesced access.  The lanes of one head form an
-// aligned power-of-two group inside the wave, so the L2 sum of squares is a
-// few lane shuffles.  Sequence starts inside a tile switch the out-of-sequence
-// taps to the caller's conv history (or zeros).
+// laid out for HBM: each lane owns 4 consecutive channels (8 bytes of bf16, 16
+// of fp32; 4 rather than 8 bf16 channels keeps the fp64 arithmetic below half
+// the register file, for occupancy) and walks a tile of consecutive tokens,
+// keeping the conv window in registers; a wave covers 256 contiguous channels
+// of a token row, so every load and store is one coalesced access.  The lanes
+// of one head form an aligned power-of-two group inside the wave, so the L2
+// sum of squares is a few lane shuffles.  Sequence starts inside a tile switch
+// the out-of-sequence taps to the caller's conv history (or zeros).
 //
 // Rounding.  With bf16 outputs every value is computed in fp64 and rounded
 // once to bf16 (nearest, ties to even), so the result is the correctly rounded
@@ -30,7 +31,10 @@ namespace kda {
 namespace {
 
 constexpr int kConvThreads = 256;
-constexpr int kConvTile = 16;  // tokens per thread
+#ifndef KDA_CONV_TILE
+#define KDA_CONV_TILE 16
+#endif
+constexpr int kConvTile = KDA_CONV_TILE;  // tokens per thread
 
 // Offset i of the packed batch, clamped to [0, total]; cu == NULL is one sequence.
 __device__ __forceinline__ int64_t seq_off(const int32_t *cu, int i, int64_t total) {
@@ -55,7 +59,46 @@ template <class T> struct ConvAcc { typedef float type; };
 template <> struct ConvAcc<bf16> { typedef double type; };
 
 __device__ __forceinline__ float silu_of(float a) { return a / (1.0f + __expf(-a)); }
-__device__ __forceinline__ double silu_of(double a) { return a / (1.0 + exp(-a)); }
+
+// e^x in fp64 for the SiLU, from the mathematics: x = n ln2 + r with n the
+// nearest integer to x / ln2 (Cody-Waite reduction: ln2 split into a 32-bit
+// head, so n * head is exact for |n| < 2^20, and a tail holding the next 53
+// bits), |r| <= ln2 / 2, then e^r by its Taylor polynomial to degree 12
+// (truncation below 2.5e-16 relative) and the scaling by 2^n.  x is clamped to
+// [-708, 708]; outside, the SiLU is already a or 0 to far below bf16 precision.
+__device__ __forceinline__ double exp_f64(double x) {
+    constexpr double kInvLn2 = 0x1.71547652b82fep+0;
+    constexpr double kLn2Hi = 0x1.62e42fee00000p-1;    // ln 2 to 32 significant bits
+    constexpr double kLn2Lo = 0x1.a39ef35793c76p-33;   // ln 2 - kLn2Hi
+    x = fmin(fmax(x, -708.0), 708.0);
+    const double n = __builtin_rint(x * kInvLn2);
+    double r = fma(-n, kLn2Hi, x);
+    r = fma(-n, kLn2Lo, r);
+    double p = 1.0 / 479001600.0;                       // 1 / 12!
+    p = fma(p, r, 1.0 / 39916800.0);
+    p = fma(p, r, 1.0 / 3628800.0);
+    p = fma(p, r, 1.0 / 362880.0);
+    p = fma(p, r, 1.0 / 40320.0);
+    p = fma(p, r, 1.0 / 5040.0);
+    p = fma(p, r, 1.0 / 720.0);
+    p = fma(p, r, 1.0 / 120.0);
+    p = fma(p, r, 1.0 / 24.0);
+    p = fma(p, r, 1.0 / 6.0);
+    p = fma(p, r, 0.5);
+    p = fma(p, r, 1.0);
+    p = fma(p, r, 1.0);
+    return __builtin_ldexp(p, (int)n);
+}
+
+// a * sigmoid(a) = a / (1 + e^{-a}) in fp64: the reciprocal from the hardware
+// estimate refined by two Newton steps (each squares the relative error).
+__device__ __forceinline__ double silu_of(double a) {
+    const double d = 1.0 + exp_f64(-a);
+    double r = __builtin_amdgcn_rcp(d);
+    r = fma(r, fma(-d, r, 1.0), r);
+    r = fma(r, fma(-d, r, 1.0), r);
+    return a * r;
+}
 __device__ __forceinline__ float inv_norm(float ss, float eps) { return 1.0f / sqrtf(ss + eps); }
 __device__ __forceinline__ double inv_norm(double ss, float eps) { return 1.0 / sqrt(ss + (double)eps); }
 __device__ __forceinline__ float store_val(float x, float) { return x; }
@@ -72,13 +115,24 @@ __device__ __forceinline__ int find_seq(const int32_t *cu, int nseq, int64_t t) 
     return lo;
 }
 
+// Channels per lane: a 16-byte vector for fp32; for bf16 a tunable 8 (16 bytes)
+// or 4 (8 bytes; fewer registers per lane for the fp64 arithmetic).
+#ifndef KDA_CONV_VEC_BF16
+#define KDA_CONV_VEC_BF16 4
+#endif
+template <class T> struct ConvVec { static constexpr int n = 4; typedef f32x4 type; };
+template <> struct ConvVec<bf16> {
+    static constexpr int n = KDA_CONV_VEC_BF16;
+    typedef bf16 type __attribute__((ext_vector_type(KDA_CONV_VEC_BF16)));
+};
+
 template <class T, int W, int LPG>  // LPG: lanes per L2 group (0 = no L2)
 __global__ __launch_bounds__(kConvThreads)
 void conv_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
                  const int32_t *__restrict__ cu_seqlens, int nseq, int64_t total, int64_t C,
                  const T *__restrict__ hist, int silu, float eps, T *__restrict__ y) {
-    constexpr int V = Vec16<T>::n;
-    typedef typename Vec16<T>::type VT;
+    constexpr int V = ConvVec<T>::n;
+    typedef typename ConvVec<T>::type VT;
     typedef typename ConvAcc<T>::type A;
     const int64_t nvec = C / V;
     const int64_t cv = (int64_t)blockIdx.x * kConvThreads + threadIdx.x;  // channel vector
@@ -109,6 +163,14 @@ void conv_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__re
     int64_t bos = seq_off(cu_seqlens, n, total);
     int64_t eos = seq_off(cu_seqlens, n + 1, total);
 
+    // The taps of token t are raw rows t-(W-1) .. t; each row is converted once
+    // and slides through `win` (win[i] holds position t-(W-1)+i).
+    A win[W][V];
+#pragma unroll
+    for (int i = 1; i < W; ++i)
+#pragma unroll
+        for (int e = 0; e < V; ++e) win[i][e] = (A)to_f32(raw[i - 1][e]);
+
 #pragma unroll
     for (int tt = 0; tt < kConvTile; ++tt) {
         const int64_t t = t0 + tt;
@@ -118,20 +180,33 @@ void conv_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__re
             bos = seq_off(cu_seqlens, n, total);
             eos = seq_off(cu_seqlens, n + 1, total);
         }
+#pragma unroll
+        for (int i = 0; i + 1 < W; ++i)
+#pragma unroll
+            for (int e = 0; e < V; ++e) win[i][e] = win[i + 1][e];
+#pragma unroll
+        for (int e = 0; e < V; ++e) win[W - 1][e] = (A)to_f32(raw[tt + W - 1][e]);
         A acc[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) acc[e] = bs[e];
+        if (t - (W - 1) >= bos) {                    // all taps inside the sequence
 #pragma unroll
-        for (int i = 0; i < W; ++i) {
-            const int64_t p = t - (W - 1) + i;
-            if (p >= bos) {
+            for (int i = 0; i < W; ++i)
 #pragma unroll
-                for (int e = 0; e < V; ++e) acc[e] += wt[i][e] * (A)to_f32(raw[tt + i][e]);
-            } else if (hist && active) {
-                const T *h = hist + ((int64_t)n * (W - 1) + (p - bos + (W - 1))) * C + c0;
-                const VT hv = *reinterpret_cast<const VT *>(h);
+                for (int e = 0; e < V; ++e) acc[e] += wt[i][e] * win[i][e];
+        } else {                                     // near a sequence start
 #pragma unroll
-                for (int e = 0; e < V; ++e) acc[e] += wt[i][e] * (A)to_f32(hv[e]);
+            for (int i = 0; i < W; ++i) {
+                const int64_t p = t - (W - 1) + i;
+                if (p >= bos) {
+#pragma unroll
+                    for (int e = 0; e < V; ++e) acc[e] += wt[i][e] * win[i][e];
+                } else if (hist && active) {
+                    const T *h = hist + ((int64_t)n * (W - 1) + (p - bos + (W - 1))) * C + c0;
+                    const VT hv = *reinterpret_cast<const VT *>(h);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) acc[e] += wt[i][e] * (A)to_f32(hv[e]);
+                }
             }
         }
         if (silu) {
@@ -187,7 +262,7 @@ template <class T, int W, int LPG>
 hipError_t launch_conv(const ConvArgs &a, hipStream_t s) {
     const int64_t C = (int64_t)a.heads * a.head_dim;
     if (a.total_tokens > 0) {
-        const int64_t nvec = C / Vec16<T>::n;
+        const int64_t nvec = C / ConvVec<T>::n;
         dim3 grid((unsigned)((nvec + kConvThreads - 1) / kConvThreads),
                   (unsigned)((a.total_tokens + kConvTile - 1) / kConvTile));
         hipLaunchKernelGGL((conv_kernel<T, W, LPG>), grid, dim3(kConvThreads), 0, s,
@@ -210,7 +285,7 @@ hipError_t launch_conv(const ConvArgs &a, hipStream_t s) {
 template <class T, int W>
 hipError_t dispatch_lpg(const ConvArgs &a, hipStream_t s) {
     if (!a.l2) return launch_conv<T, W, 0>(a, s);
-    switch (a.head_dim / Vec16<T>::n) {
+    switch (a.head_dim / ConvVec<T>::n) {
         case 1: return launch_conv<T, W, 1>(a, s);
         case 2: return launch_conv<T, W, 2>(a, s);
         case 4: return launch_conv<T, W, 4>(a, s);

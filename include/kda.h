@@ -91,10 +91,9 @@ typedef enum {
  *                  sequence (history included when the sequence is shorter).
  *                  May alias conv_state_in.
  *   y              [total_tokens, num_heads, head_dim]     dtype; must not alias x.
- * Supported: width in 1..4; head_dim a multiple of the 16-byte vector (8 bf16 /
- * 4 fp32); with l2_normalize, head_dim / vector must be a power of two <= 64
- * (head_dim <= 512 bf16 / 256 fp32); total_tokens >= 0 (0 enqueues only the
- * state copy).
+ * Supported: width in 1..4; head_dim a multiple of 4 (a lane of the kernel
+ * owns 4 channels); with l2_normalize, head_dim / 4 must be a power of two
+ * <= 64 (head_dim <= 256); total_tokens >= 0 (0 enqueues only the state copy).
  */
 KDA_API kda_status_t kda_short_conv(const void *x, const void *weight, const void *bias,
                             const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,

@@ -129,9 +129,10 @@ def conv(lib, **kw):
     (dict(eps=-1.0), kda.KDA_ERR_INVALID_ARG),
     (dict(W=5), kda.KDA_ERR_UNSUPPORTED),
     (dict(W=0), kda.KDA_ERR_UNSUPPORTED),
-    (dict(D=12), kda.KDA_ERR_UNSUPPORTED),           # not a multiple of 8 bf16
-    (dict(D=24), kda.KDA_ERR_UNSUPPORTED),           # 3 vectors per head: not a power of two
-    (dict(D=1024), kda.KDA_ERR_UNSUPPORTED),         # 128 vectors per head
+    (dict(D=6), kda.KDA_ERR_UNSUPPORTED),            # not a multiple of 4 channels
+    (dict(D=12), kda.KDA_ERR_UNSUPPORTED),           # 3 lanes per head: not a power of two
+    (dict(D=24), kda.KDA_ERR_UNSUPPORTED),           # 6 lanes per head: not a power of two
+    (dict(D=512), kda.KDA_ERR_UNSUPPORTED),          # 128 lanes per head
 ])
 def test_short_conv_rejects(lib, kw, status):
     assert conv(lib, **kw) == status
