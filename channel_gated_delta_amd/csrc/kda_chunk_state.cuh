@@ -388,18 +388,24 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
             }
 
             // prefix of the row-group sums (lanes rg*CPW + i share a channel pair)
-            float inc0 = a0, inc1 = a1;
+            float inc0 = a0, inc1 = a1, tot0, tot1;
+            if constexpr (CPW == 16 && RG == 4) {   // row groups are the 16-lane rows
+                rows4_prefix(a0, rg, inc0, tot0);
+                rows4_prefix(a1, rg, inc1, tot1);
+            } else {
 #pragma unroll
-            for (int d = 1; d < RG; d <<= 1) {
-                const float u0 = __shfl_up(inc0, d * CPW, kWave);
-                const float u1 = __shfl_up(inc1, d * CPW, kWave);
-                if (rg >= d) {
-                    inc0 += u0;
-                    inc1 += u1;
+                for (int d = 1; d < RG; d <<= 1) {
+                    const float u0 = __shfl_up(inc0, d * CPW, kWave);
+                    const float u1 = __shfl_up(inc1, d * CPW, kWave);
+                    if (rg >= d) {
+                        inc0 += u0;
+                        inc1 += u1;
+                    }
                 }
+                const int lastl = (RG - 1) * CPW + (lane % CPW);
+                tot0 = __shfl(inc0, lastl, kWave);
+                tot1 = __shfl(inc1, lastl, kWave);
             }
-            const int lastl = (RG - 1) * CPW + (lane % CPW);
-            const float tot0 = __shfl(inc0, lastl, kWave), tot1 = __shfl(inc1, lastl, kWave);
             const float off0 = inc0 - a0, off1 = inc1 - a1;
 
             if (act) {

@@ -48,18 +48,82 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Sum over groups of `width` consecutive lanes (width a power of two <= 64).
+// ---------------------------------------------------------------------------
+// Cross-lane sums without the LDS: DPP moves inside a row of 16 lanes
+// (quad_perm [1,0,3,2] and [2,3,0,1] pair lanes l^1 and l^2; row_half_mirror
+// pairs quad 0 with quad 1 of each 8-lane half, row_mirror the two halves of a
+// row) and the gfx950 permlane swaps across rows (16-lane rows swapped in pairs,
+// 32-lane halves swapped).  Every lane of a group ends with the same sum.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) { return __uint_as_float(dpp_mov<CTRL>(__float_as_uint(v))); }
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const uint64_t u = __double_as_longlong(v);
+    const uint64_t lo = dpp_mov<CTRL>((uint32_t)u), hi = dpp_mov<CTRL>((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)(lo | (hi << 32)));
+}
+// (row pair) swap: element 0 holds this lane's value for even rows / the even
+// row's for odd rows, element 1 the odd row's; their sum is the pair's sum.
+__device__ __forceinline__ float rowpair_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float halves_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ double rowpair_sum(double v) {
+    const uint64_t u = __double_as_longlong(v);
+    const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    return __longlong_as_double((long long)(a[0] | ((uint64_t)b[0] << 32))) +
+           __longlong_as_double((long long)(a[1] | ((uint64_t)b[1] << 32)));
+}
+__device__ __forceinline__ double halves_sum(double v) {
+    const uint64_t u = __double_as_longlong(v);
+    const auto a = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    return __longlong_as_double((long long)(a[0] | ((uint64_t)b[0] << 32))) +
+           __longlong_as_double((long long)(a[1] | ((uint64_t)b[1] << 32)));
+}
+
+// Sum over aligned groups of `width` consecutive lanes (width a power of two <= 64).
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int off = width / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, width);
+    if constexpr (width >= 2) v += dpp_f<0xB1>(v);
+    if constexpr (width >= 4) v += dpp_f<0x4E>(v);
+    if constexpr (width >= 8) v += dpp_f<0x141>(v);
+    if constexpr (width >= 16) v += dpp_f<0x140>(v);
+    if constexpr (width >= 32) v = rowpair_sum(v);
+    if constexpr (width >= 64) v = halves_sum(v);
     return v;
 }
 template <int width>
 __device__ __forceinline__ double group_sum(double v) {
-#pragma unroll
-    for (int off = width / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, width);
+    if constexpr (width >= 2) v += dpp_d<0xB1>(v);
+    if constexpr (width >= 4) v += dpp_d<0x4E>(v);
+    if constexpr (width >= 8) v += dpp_d<0x141>(v);
+    if constexpr (width >= 16) v += dpp_d<0x140>(v);
+    if constexpr (width >= 32) v = rowpair_sum(v);
+    if constexpr (width >= 64) v = halves_sum(v);
     return v;
+}
+
+// Inclusive prefix and total over the four 16-lane rows of a wave, lane by lane
+// (row r of the result holds a_0 + .. + a_r of the same lane index).
+__device__ __forceinline__ void rows4_prefix(float a, int row, float &incl, float &total) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+    const float p0 = __uint_as_float(p[0]), pair = p0 + __uint_as_float(p[1]);
+    const float x = (row & 1) ? a + p0 : a;
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+    const float q0 = __uint_as_float(q[0]);
+    incl = row >= 2 ? x + q0 : x;
+    total = q0 + __uint_as_float(q[1]);
 }
 
 // ---------------------------------------------------------------------------
