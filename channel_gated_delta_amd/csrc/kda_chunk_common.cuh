@@ -40,6 +40,17 @@ template <class T> struct Pair;
 template <> struct Pair<bf16> { typedef bf16x2 type; };
 template <> struct Pair<float> { typedef f32x2 type; };
 
+// Load / store at a uniform base plus a 32-bit byte offset (lets the compiler use
+// the scalar-base + vector-offset addressing form instead of 64-bit address math).
+template <class V>
+__device__ __forceinline__ V ld_off(const void *base, uint32_t byte_off) {
+    return *reinterpret_cast<const V *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+template <class V>
+__device__ __forceinline__ void st_off(void *base, uint32_t byte_off, V x) {
+    *reinterpret_cast<V *>(reinterpret_cast<char *>(base) + byte_off) = x;
+}
+
 // Packed-sequence offset i clamped to [0, total]; cu == NULL is one sequence.
 __device__ __forceinline__ int64_t chunk_seq_off(const int32_t *cu, int i, int64_t total) {
     if (!cu) return i == 0 ? 0 : total;

@@ -93,7 +93,7 @@ __device__ __forceinline__ BReg4 low_half(const BReg8 &b) {
 // their first use, which would expose the LDS latency at every product).
 template <int DK, int C, int LDK, int LDC, int LDV>
 __device__ __forceinline__ void state_chain_bf16(
-    f32x4 (&Sacc)[DK / 16], f32x4 (&Ot)[C / 16], const bf16 *sQdh, const bf16 *sQdl,
+    f32x4 (&Sacc)[DK / 16], BReg8 (&sb)[DK / 32], f32x4 (&Ot)[C / 16], const bf16 *sQdh, const bf16 *sQdl,
     const bf16 *sKdh, const bf16 *sKdl, const bf16 *sKrTh, const bf16 *sKrTl, const bf16 *sTbh,
     const bf16 *sTbl, const bf16 *sPh, const bf16 *sPl, const float *sV, const float *sEGn,
     int wcol, int lane) {
@@ -117,18 +117,19 @@ __device__ __forceinline__ void state_chain_bf16(
         fk[0][R] = lda8(sKdh, sKdl, LDK, R * 16, 0, lane);
         fq[0][R] = lda8(sQdh, sQdl, LDK, R * 16, 0, lane);
     }
-    // the state as B operand (hi, lo)
-    BReg8 sb[NKB];
-#pragma unroll
-    for (int j = 0; j < NKB; ++j) sb[j] = breg8(Sacc[2 * j], Sacc[2 * j + 1]);
+    // sb holds the state as B operand (hi, lo), split at the end of the previous step
 
-    // E = Kd S, O = Qd S: k-block j's products while block j+1 loads
-    f32x4 Et[NTC];
+    // E = Kd S, O = Qd S: k-block j's products while block j+1 loads.  The three
+    // split terms go to separate accumulators (summed at the end), so 6 NTC
+    // independent accumulation chains interleave.
+    f32x4 Et3[3][NTC], Ot3[3][NTC];
 #pragma unroll
-    for (int R = 0; R < NTC; ++R) {
-        Et[R] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Ot[R] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int R = 0; R < NTC; ++R) {
+            Et3[t][R] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Ot3[t][R] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
     for (int j = 0; j < NKB; ++j) {
         const int cur = j & 1, nxt = cur ^ 1;
@@ -144,21 +145,23 @@ __device__ __forceinline__ void state_chain_bf16(
         // for the one before it
 #pragma unroll
         for (int R = 0; R < NTC; ++R) {
-            Et[R] = mma(fk[cur][R].h, sb[j].h, Et[R]);
-            Ot[R] = mma(fq[cur][R].h, sb[j].h, Ot[R]);
-        }
-#pragma unroll
-        for (int R = 0; R < NTC; ++R) {
-            Et[R] = mma(fk[cur][R].h, sb[j].l, Et[R]);
-            Ot[R] = mma(fq[cur][R].h, sb[j].l, Ot[R]);
-        }
-#pragma unroll
-        for (int R = 0; R < NTC; ++R) {
-            Et[R] = mma(fk[cur][R].l, sb[j].h, Et[R]);
-            Ot[R] = mma(fq[cur][R].l, sb[j].h, Ot[R]);
+            Et3[0][R] = mma(fk[cur][R].h, sb[j].h, Et3[0][R]);
+            Ot3[0][R] = mma(fq[cur][R].h, sb[j].h, Ot3[0][R]);
+            Et3[1][R] = mma(fk[cur][R].h, sb[j].l, Et3[1][R]);
+            Ot3[1][R] = mma(fq[cur][R].h, sb[j].l, Ot3[1][R]);
+            Et3[2][R] = mma(fk[cur][R].l, sb[j].h, Et3[2][R]);
+            Ot3[2][R] = mma(fq[cur][R].l, sb[j].h, Ot3[2][R]);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
+    f32x4 Et[NTC];
+#pragma unroll
+    for (int R = 0; R < NTC; ++R)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            Et[R][r] = Et3[0][R][r] + (Et3[1][R][r] + Et3[2][R][r]);
+            Ot[R][r] = Ot3[0][R][r] + (Ot3[1][R][r] + Ot3[2][R][r]);
+        }
     // first half of the state-update fragments load during the U and P U products
     constexpr int NK1 = NTK / 2;
     AF8 fr8[NTK];
@@ -223,6 +226,9 @@ __device__ __forceinline__ void state_chain_bf16(
 #pragma unroll
         for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr4[rt].l, ub4.h, Sacc[rt]);
     }
+    // split the new state for the next step now: it overlaps the step barrier
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) sb[j] = breg8(Sacc[2 * j], Sacc[2 * j + 1]);
 }
 
 template <class T, class TO, int DK, int BV, int C>
@@ -293,26 +299,26 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                 for (int j = 0; j < RP; ++j) {
                     const uint32_t off = (uint32_t)min(rg * RP + j, last) * (uint32_t)rowQK +
                                          (uint32_t)(2 * cpair);
-                    R.q[j] = *reinterpret_cast<const T2 *>(qb + off);
-                    R.k[j] = *reinterpret_cast<const T2 *>(kb + off);
-                    R.g[j] = *reinterpret_cast<const f32x2 *>(gb + off);
+                    R.q[j] = ld_off<T2>(qb, off * (uint32_t)sizeof(T));
+                    R.k[j] = ld_off<T2>(kb, off * (uint32_t)sizeof(T));
+                    R.g[j] = ld_off<f32x2>(gb, off * 4u);
                 }
             }
             const float *tbb = tb + ((size_t)cs * H + h) * C, *pmb = pm + ((size_t)cs * H + h) * C;
-            const uint32_t wo = (uint32_t)min(tr, last) * (uint32_t)(H * C) + (uint32_t)tc;
+            const uint32_t wo = ((uint32_t)min(tr, last) * (uint32_t)(H * C) + (uint32_t)tc) * 4u;
             if constexpr (NTB == 1) {
-                R.tb[0][0] = tbb[wo];
-                R.pm[0][0] = pmb[wo];
+                R.tb[0][0] = ld_off<float>(tbb, wo);
+                R.pm[0][0] = ld_off<float>(pmb, wo);
             } else {
 #pragma unroll
                 for (int j = 0; j < NTB4; ++j) {
-                    R.tb[j] = *reinterpret_cast<const f32x4 *>(tbb + wo + 4 * j);
-                    R.pm[j] = *reinterpret_cast<const f32x4 *>(pmb + wo + 4 * j);
+                    R.tb[j] = ld_off<f32x4>(tbb, wo + 16u * j);
+                    R.pm[j] = ld_off<f32x4>(pmb, wo + 16u * j);
                 }
             }
             const T *vb = v + (size_t)cs * rowV + (size_t)h * DV + v0;
-            R.v = *reinterpret_cast<const TV *>(vb + (uint32_t)min(vr, last) * (uint32_t)rowV +
-                                                (uint32_t)vcol);
+            R.v = ld_off<TV>(vb, ((uint32_t)min(vr, last) * (uint32_t)rowV + (uint32_t)vcol) *
+                                     (uint32_t)sizeof(T));
         };
 
         // Step s: build stage s & 1 from chunk s (if s < nchunks) out of `cur`, and
@@ -464,6 +470,13 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                     Sacc[rt][r] = src[(size_t)(rt * 16 + acc_row(lane, r)) * DV + vc];
             }
         }
+        // the state split into (hi, lo) B operands, refreshed at the end of each chain
+        constexpr int NKB = DK / 32 > 0 ? DK / 32 : 1;
+        BReg8 sbs[NKB];
+        if constexpr (SPLIT && DK % 32 == 0) {
+#pragma unroll
+            for (int j = 0; j < NKB; ++j) sbs[j] = breg8(Sacc[2 * j], Sacc[2 * j + 1]);
+        }
         for (int s = 0; s < nsteps; ++s) {
             if (s >= 1 && s <= nchunks && owner) {
                 const int64_t c0 = bos + (int64_t)(s - 1) * C;
@@ -484,17 +497,19 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
 
                 if constexpr (SPLIT && DK % 32 == 0 && (C == 16 || C == 32)) {
                     f32x4 Ot[NTC];
-                    state_chain_bf16<DK, C, LDK, LDC, LDV>(Sacc, Ot, sQdh, sQdl, sKdh, sKdl, sKrTh,
-                                                           sKrTl, sTbh, sTbl, sPh, sPl, sV, sEGn,
-                                                           wave * 16, lane);
+                    state_chain_bf16<DK, C, LDK, LDC, LDV>(Sacc, sbs, Ot, sQdh, sQdl, sKdh, sKdl,
+                                                           sKrTh, sKrTl, sTbh, sTbl, sPh, sPl, sV,
+                                                           sEGn, wave * 16, lane);
+                    TO *ob = o + (size_t)c0 * rowV + (size_t)h * DV;
 #pragma unroll
                     for (int R = 0; R < NTC; ++R)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int row = R * 16 + acc_row(lane, r);
                             if (row < nt)
-                                o[(size_t)(c0 + row) * rowV + (size_t)h * DV + vc] =
-                                    from_f32<TO>(Ot[R][r]);
+                                st_off<TO>(ob, ((uint32_t)row * (uint32_t)rowV + (uint32_t)vc) *
+                                                   (uint32_t)sizeof(TO),
+                                           from_f32<TO>(Ot[R][r]));
                         }
                 } else {
                 RegB<T, NTK> Sb;
