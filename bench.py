@@ -259,7 +259,7 @@ def main():
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 (fp32 accumulate, split-bf16 products, fp32 state and o)",
+        "dtype": "bf16",
         "data": "synthetic (seeded; no weights or datasets)",
         "config": {"workload": spec.name, "batch": N, "seq_len": T, "heads": H, "dk": DK,
                    "dv": DV, "chunk": spec.chunk, "path": "3x short_conv (conv4+SiLU, q/k L2) + "
