@@ -16,12 +16,15 @@
 // sum of squares is a few lane shuffles.  Sequence starts inside a tile switch
 // the out-of-sequence taps to the caller's conv history (or zeros).
 //
-// Rounding.  With bf16 outputs every value is computed in fp64 and rounded
-// once to bf16 (nearest, ties to even), so the result is the correctly rounded
-// conv/SiLU/L2 value; an fp32 evaluation would round a value lying within its
-// own error of a bf16 rounding midpoint to either side, and such 1-ulp flips of
-// q and k move the recurrence's largest outputs by far more than one ulp.  With
-// fp32 outputs the arithmetic is fp32.
+// Rounding.  With bf16 outputs every value is rounded once to bf16 (nearest,
+// ties to even) from its exact conv/SiLU/L2 value, i.e. the result is correctly
+// rounded: a plain fp32 evaluation would round a value lying within its own
+// error of a bf16 rounding midpoint to either side, and such 1-ulp flips of q
+// and k move the recurrence's largest outputs by far more than one ulp.  The
+// conv is exact in fp64; the sigmoid and the norm take a fast route with a
+// proven error bound, and the few tokens whose result the bound cannot place on
+// one side of a midpoint are redone in full fp64.  With fp32 outputs the
+// arithmetic is fp32.
 #include <type_traits>
 
 #include "kda_device.cuh"
@@ -101,8 +104,40 @@ __device__ __forceinline__ double silu_of(double a) {
 }
 __device__ __forceinline__ float inv_norm(float ss, float eps) { return 1.0f / sqrtf(ss + eps); }
 __device__ __forceinline__ double inv_norm(double ss, float eps) { return 1.0 / sqrt(ss + (double)eps); }
-__device__ __forceinline__ float store_val(float x, float) { return x; }
-__device__ __forceinline__ bf16 store_val(double x, bf16) { return bf16_from_f64(x); }
+
+// Sigmoid 1 / (1 + e^-a) to within 1.8 u relative (u = 2^-24) for a >= -80, at a
+// fraction of the fp64 cost: e^-a = 2^x with x = -a log2 e split in fp64 into an
+// integer n and |f| <= 1/2 (f exact), 2^f from the hardware exp2 (below 0.77 fp32
+// ulp on that range, i.e. 1.54 u relative) of f rounded to fp32 (0.17 u more),
+// scaled by 2^n exactly; the reciprocal of 1 + e^-a from the hardware estimate
+// refined by one Newton step in fp64 (error squared to below 2^-44).  An error
+// eta in e^-a reaches the sigmoid as eta (1 - sigmoid) <= eta.  For a < -80 the
+// fp32 estimates leave their range and the result means nothing.
+__device__ __forceinline__ double sigmoid_fast(double a) {
+    const double x = a * -0x1.71547652b82fep+0;
+    const double n = __builtin_rint(x);
+    const float f = (float)(x - n);
+    const double e = __builtin_ldexp((double)__builtin_amdgcn_exp2f(f), (int)n);
+    const double d = 1.0 + e;
+    const double r = (double)__builtin_amdgcn_rcpf((float)d);
+    return fma(r, fma(-d, r, 1.0), r);
+}
+
+// s^(-1/2) for 2^-100 <= s <= 2^100: the hardware estimate and one Newton step
+// in fp64 (relative error below 2^-42).
+__device__ __forceinline__ double rsqrt_fast(double s) {
+    const double r = (double)__builtin_amdgcn_rsqf((float)s);
+    return r * fma(-0.5 * s * r, r, 1.5);
+}
+
+// Whether an fp32 value known to lie within 5 of its ulps of the exact result
+// rounds to the same bf16 as that result: its 16 bits below the bf16 precision
+// must be more than 6 ulps away from the rounding midpoint 0x8000.  (Binade
+// edges are 0x8000 ulps away from any midpoint, and both signs round alike.)
+__device__ __forceinline__ bool bf16_rounding_sure(float v) {
+    const uint32_t low = __float_as_uint(v) & 0xffffu;
+    return low - (0x8000u - 6u) > 12u;
+}
 
 // Sequence containing token t: the largest n with cu[n] <= t.
 __device__ __forceinline__ int find_seq(const int32_t *cu, int nseq, int64_t t) {
@@ -209,25 +244,76 @@ void conv_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__re
                 }
             }
         }
-        if (silu) {
+        VT out;
+        if constexpr (std::is_same<T, bf16>::value) {
+            // Fast path: sigmoid_fast, an fp64 sum of squares and rsqrt_fast.  Each
+            // y carries at most 1.8 u relative error from its sigmoid, the norm at
+            // most the largest of those over the head, so the fp32 rounding of the
+            // result lies within 2 * 1.8 u * 2^24 + 1/2 < 4.2 fp32 ulps of the exact
+            // value and rounds to the correctly rounded bf16 whenever
+            // bf16_rounding_sure says so.  Otherwise (about 1 token in 20 per wave)
+            // the wave redoes the token in fp64.
+            A yv[V];
+            bool unsure = false;
 #pragma unroll
-            for (int e = 0; e < V; ++e) acc[e] = silu_of(acc[e]);
+            for (int e = 0; e < V; ++e) {
+                yv[e] = silu ? acc[e] * sigmoid_fast(acc[e]) : acc[e];
+                unsure |= silu && acc[e] < -80.0;
+            }
+            if constexpr (LPG > 0) {
+                A ss = 0;
+#pragma unroll
+                for (int e = 0; e < V; ++e) ss += yv[e] * yv[e];
+                const double s = group_sum<LPG>(ss) + (double)eps;
+                unsure |= !(s >= 0x1p-100 && s <= 0x1p100);
+                const double inv = rsqrt_fast(s);
+#pragma unroll
+                for (int e = 0; e < V; ++e) yv[e] *= inv;
+            }
+            float yf[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                yf[e] = (float)yv[e];
+                unsure |= !bf16_rounding_sure(yf[e]);
+            }
+            if (__builtin_amdgcn_ballot_w64(unsure && active) != 0) {
+                if (silu) {
+#pragma unroll
+                    for (int e = 0; e < V; ++e) acc[e] = silu_of(acc[e]);
+                }
+                if constexpr (LPG > 0) {
+                    A ss = 0;
+#pragma unroll
+                    for (int e = 0; e < V; ++e) ss += acc[e] * acc[e];
+                    ss = group_sum<LPG>(ss);
+                    const A inv = inv_norm(ss, eps);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) acc[e] *= inv;
+                }
+#pragma unroll
+                for (int e = 0; e < V; ++e) out[e] = bf16_from_f64(acc[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e) out[e] = (bf16)yf[e];
+            }
+        } else {
+            if (silu) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) acc[e] = silu_of(acc[e]);
+            }
+            if constexpr (LPG > 0) {
+                A ss = 0;
+#pragma unroll
+                for (int e = 0; e < V; ++e) ss += acc[e] * acc[e];
+                ss = group_sum<LPG>(ss);
+                const A inv = inv_norm(ss, eps);
+#pragma unroll
+                for (int e = 0; e < V; ++e) acc[e] *= inv;
+            }
+#pragma unroll
+            for (int e = 0; e < V; ++e) out[e] = acc[e];
         }
-        if constexpr (LPG > 0) {
-            A ss = 0;
-#pragma unroll
-            for (int e = 0; e < V; ++e) ss += acc[e] * acc[e];
-            ss = group_sum<LPG>(ss);
-            const A inv = inv_norm(ss, eps);
-#pragma unroll
-            for (int e = 0; e < V; ++e) acc[e] *= inv;
-        }
-        if (active) {
-            VT out;
-#pragma unroll
-            for (int e = 0; e < V; ++e) out[e] = store_val(acc[e], T());
-            *reinterpret_cast<VT *>(y + t * C + c0) = out;
-        }
+        if (active) *reinterpret_cast<VT *>(y + t * C + c0) = out;
     }
 }
 
