@@ -38,6 +38,20 @@ constexpr int kConvThreads = 256;
 #define KDA_CONV_TILE 16
 #endif
 constexpr int kConvTile = KDA_CONV_TILE;  // tokens per thread
+// Workgroups per CU the register allocation must allow (4 = 4 waves per SIMD):
+// the straight-line interior tile would otherwise trade occupancy for
+// instruction-level parallelism far beyond what pays.
+#ifndef KDA_CONV_MINB
+#define KDA_CONV_MINB 4
+#endif
+#ifndef KDA_CONV_GROUP
+#define KDA_CONV_GROUP 2
+#endif
+constexpr int kConvGroup = KDA_CONV_GROUP;
+#ifndef KDA_CONV_AHEAD
+#define KDA_CONV_AHEAD 4
+#endif
+constexpr int kConvAhead = KDA_CONV_AHEAD;  // rows loaded this many tokens ahead of use
 
 // Offset i of the packed batch, clamped to [0, total]; cu == NULL is one sequence.
 __device__ __forceinline__ int64_t seq_off(const int32_t *cu, int i, int64_t total) {
@@ -161,11 +175,105 @@ template <> struct ConvVec<bf16> {
     typedef bf16 type __attribute__((ext_vector_type(KDA_CONV_VEC_BF16)));
 };
 
-template <class T, int W, int LPG>  // LPG: lanes per L2 group (0 = no L2)
-__global__ __launch_bounds__(kConvThreads)
+typedef ConvVec<bf16>::type BfVec;
+constexpr int kBfVec = ConvVec<bf16>::n;
+
+// Fast finish of one bf16 token row: sigmoid_fast, an fp64 sum of squares over
+// the head and rsqrt_fast.  Each y carries at most 1.8 u relative error from its
+// sigmoid and the norm at most the largest of those over the head, so the fp32
+// rounding of the result lies within 2 * 1.8 u * 2^24 + 1/2 < 4.2 fp32 ulps of
+// the exact value and rounds to the correctly rounded bf16 whenever
+// bf16_rounding_sure says so.  Returns whether this lane has a value it cannot
+// vouch for (then the token must be redone by finish_exact).
+template <int LPG>
+__device__ __forceinline__ bool finish_fast(const double (&acc)[kBfVec], bool silu, float eps,
+                                            BfVec &out) {
+    double yv[kBfVec];
+    bool unsure = false;
+#pragma unroll
+    for (int e = 0; e < kBfVec; ++e) {
+        yv[e] = silu ? acc[e] * sigmoid_fast(acc[e]) : acc[e];
+        unsure |= silu && acc[e] < -80.0;
+    }
+    if constexpr (LPG > 0) {
+        double ss = 0;
+#pragma unroll
+        for (int e = 0; e < kBfVec; ++e) ss += yv[e] * yv[e];
+        const double s = group_sum<LPG>(ss) + (double)eps;
+        unsure |= !(s >= 0x1p-100 && s <= 0x1p100);
+        const double inv = rsqrt_fast(s);
+#pragma unroll
+        for (int e = 0; e < kBfVec; ++e) yv[e] *= inv;
+    }
+#pragma unroll
+    for (int e = 0; e < kBfVec; ++e) {
+        const float yf = (float)yv[e];
+        unsure |= !bf16_rounding_sure(yf);
+        out[e] = (bf16)yf;
+    }
+    return unsure;
+}
+
+// The same token row entirely in fp64 (all lanes of each head group take part).
+template <int LPG>
+__device__ __forceinline__ void finish_exact(double (&acc)[kBfVec], bool silu, float eps,
+                                             BfVec &out) {
+    if (silu) {
+#pragma unroll
+        for (int e = 0; e < kBfVec; ++e) acc[e] = silu_of(acc[e]);
+    }
+    if constexpr (LPG > 0) {
+        double ss = 0;
+#pragma unroll
+        for (int e = 0; e < kBfVec; ++e) ss += acc[e] * acc[e];
+        ss = group_sum<LPG>(ss);
+        const double inv = inv_norm(ss, eps);
+#pragma unroll
+        for (int e = 0; e < kBfVec; ++e) acc[e] *= inv;
+    }
+#pragma unroll
+    for (int e = 0; e < kBfVec; ++e) out[e] = bf16_from_f64(acc[e]);
+}
+
+// A row of V channels at a 32-bit byte offset from a uniform base (the scalar
+// base + vector offset addressing form).
+template <class VT>
+__device__ __forceinline__ VT ld_row(const void *base, uint32_t byte_off) {
+    return *reinterpret_cast<const VT *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+template <class VT>
+__device__ __forceinline__ void st_row(void *base, uint32_t byte_off, VT v) {
+    *reinterpret_cast<VT *>(reinterpret_cast<char *>(base) + byte_off) = v;
+}
+
+// Fp32 finish of one token row (fp32 outputs): SiLU and the head's L2 norm.
+template <int LPG>
+__device__ __forceinline__ void finish_plain(float (&acc)[4], bool silu, float eps, f32x4 &out) {
+    if (silu) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = silu_of(acc[e]);
+    }
+    if constexpr (LPG > 0) {
+        float ss = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += acc[e] * acc[e];
+        const float inv = inv_norm(group_sum<LPG>(ss), eps);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= inv;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = acc[e];
+}
+
+// LPG: lanes per L2 group (0 = no L2).  SILU: 0 or 1 fixes the activation at
+// compile time; -1 takes the run-time flag.
+template <class T, int W, int LPG, int SILU>
+__global__ __launch_bounds__(kConvThreads, KDA_CONV_MINB)
 void conv_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
                  const int32_t *__restrict__ cu_seqlens, int nseq, int64_t total, int64_t C,
-                 const T *__restrict__ hist, int silu, float eps, T *__restrict__ y) {
+                 const T *__restrict__ hist, int silu_flag, float eps, T *__restrict__ y) {
+    constexpr bool kBf16 = std::is_same<T, bf16>::value;
+    const bool silu = SILU < 0 ? silu_flag != 0 : SILU != 0;
     constexpr int V = ConvVec<T>::n;
     typedef typename ConvVec<T>::type VT;
     typedef typename ConvAcc<T>::type A;
@@ -183,135 +291,120 @@ void conv_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__re
         for (int i = 0; i < W; ++i) wt[i][e] = active ? (A)to_f32(w[(c0 + e) * W + i]) : (A)0;
     }
 
-    // Raw rows t0-(W-1) .. t0+TT-1 (rows outside [0, total) are never used as data).
-    VT raw[kConvTile + W - 1];
-#pragma unroll
-    for (int r = 0; r < kConvTile + W - 1; ++r) {
-        const int64_t p = t0 - (W - 1) + r;
-        if (active && p >= 0 && p < total)
-            raw[r] = *reinterpret_cast<const VT *>(x + p * C + c0);
-        else
-            raw[r] = VT{};
-    }
-
     int n = find_seq(cu_seqlens, nseq, t0 < total ? t0 : total - 1);
     int64_t bos = seq_off(cu_seqlens, n, total);
     int64_t eos = seq_off(cu_seqlens, n + 1, total);
 
-    // The taps of token t are raw rows t-(W-1) .. t; each row is converted once
-    // and slides through `win` (win[i] holds position t-(W-1)+i).
-    A win[W][V];
+    // Interior tile (the common case): every lane of the block is in range and
+    // every tap of the tile's tokens lies inside one sequence, so the tile is
+    // straight-line code.  Rows are read kConvAhead tokens ahead of use, converted
+    // once, and slide through `win` (win[i] holds position t-(W-1)+i).  With bf16
+    // outputs each token is finished on the fast route and stored; the tokens
+    // where some lane could not vouch for its value are then redone in fp64 and
+    // stored again (same lane, same address: the later store wins).
+    if ((int64_t)(blockIdx.x + 1) * kConvThreads <= nvec && t0 - (W - 1) >= bos &&
+        t0 + kConvTile <= eos && C * (kConvTile + W) * (int64_t)sizeof(T) < (1ll << 31)) {
+        constexpr int R = kConvTile + W - 1;          // rows t0-(W-1) .. t0+TT-1
+        const T *xb = x + (t0 - (W - 1)) * C;
+        T *yb = y + t0 * C;
+        const uint32_t lane_off = (uint32_t)c0 * (uint32_t)sizeof(T);
+        const uint32_t row_bytes = (uint32_t)C * (uint32_t)sizeof(T);
+        VT raw[R];
 #pragma unroll
-    for (int i = 1; i < W; ++i)
+        for (int r = 0; r < W - 1 + kConvAhead && r < R; ++r)
+            raw[r] = ld_row<VT>(xb, lane_off + r * row_bytes);
+        A win[W][V];
 #pragma unroll
-        for (int e = 0; e < V; ++e) win[i][e] = (A)to_f32(raw[i - 1][e]);
+        for (int i = 1; i < W; ++i)
+#pragma unroll
+            for (int e = 0; e < V; ++e) win[i][e] = (A)to_f32(raw[i - 1][e]);
+        uint32_t flags = 0;
+#pragma unroll
+        for (int tt = 0; tt < kConvTile; ++tt) {
+            constexpr int kNext = W - 1 + kConvAhead;
+            if (tt + kNext < R) raw[tt + kNext] = ld_row<VT>(xb, lane_off + (tt + kNext) * row_bytes);
+#pragma unroll
+            for (int i = 0; i + 1 < W; ++i)
+#pragma unroll
+                for (int e = 0; e < V; ++e) win[i][e] = win[i + 1][e];
+#pragma unroll
+            for (int e = 0; e < V; ++e) win[W - 1][e] = (A)to_f32(raw[tt + W - 1][e]);
+            A acc[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                acc[e] = bs[e];
+#pragma unroll
+                for (int i = 0; i < W; ++i) acc[e] += wt[i][e] * win[i][e];
+            }
+            VT out;
+            if constexpr (kBf16)
+                flags |= (uint32_t)finish_fast<LPG>(acc, silu, eps, out) << tt;
+            else
+                finish_plain<LPG>(acc, silu, eps, out);
+            st_row<VT>(yb, lane_off + tt * row_bytes, out);
+            // Scheduling regions of kConvGroup tokens: interleaving neighbouring
+            // tokens hides latency; hoisting work across the whole tile only
+            // raises register pressure.
+            if ((tt + 1) % kConvGroup == 0) __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (kBf16) {
+#pragma unroll 1
+            for (int tt = 0; tt < kConvTile; ++tt) {
+                if (__builtin_amdgcn_ballot_w64((flags >> tt) & 1u) != 0) {
+                    A acc[V];
+#pragma unroll
+                    for (int e = 0; e < V; ++e) acc[e] = bs[e];
+#pragma unroll
+                    for (int i = 0; i < W; ++i) {
+                        const VT r = ld_row<VT>(xb, lane_off + (tt + i) * row_bytes);
+#pragma unroll
+                        for (int e = 0; e < V; ++e) acc[e] += wt[i][e] * (A)to_f32(r[e]);
+                    }
+                    VT out;
+                    finish_exact<LPG>(acc, silu, eps, out);
+                    st_row<VT>(yb, lane_off + tt * row_bytes, out);
+                }
+            }
+        }
+        return;
+    }
 
-#pragma unroll
+    // General tile (a sequence start near or inside the tile, a ragged channel
+    // block, the end of the batch): one token at a time, each tap read directly,
+    // from the batch or, before the sequence start, from the caller's conv
+    // history (zeros without one).
+#pragma unroll 1
     for (int tt = 0; tt < kConvTile; ++tt) {
         const int64_t t = t0 + tt;
-        if (t >= total) break;                      // uniform across the block
+        if (t >= total) break;                       // uniform across the block
         while (t >= eos && n + 1 < nseq) {           // next (possibly empty) sequence
             ++n;
             bos = seq_off(cu_seqlens, n, total);
             eos = seq_off(cu_seqlens, n + 1, total);
         }
-#pragma unroll
-        for (int i = 0; i + 1 < W; ++i)
-#pragma unroll
-            for (int e = 0; e < V; ++e) win[i][e] = win[i + 1][e];
-#pragma unroll
-        for (int e = 0; e < V; ++e) win[W - 1][e] = (A)to_f32(raw[tt + W - 1][e]);
         A acc[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) acc[e] = bs[e];
-        if (t - (W - 1) >= bos) {                    // all taps inside the sequence
 #pragma unroll
-            for (int i = 0; i < W; ++i)
-#pragma unroll
-                for (int e = 0; e < V; ++e) acc[e] += wt[i][e] * win[i][e];
-        } else {                                     // near a sequence start
-#pragma unroll
-            for (int i = 0; i < W; ++i) {
-                const int64_t p = t - (W - 1) + i;
-                if (p >= bos) {
-#pragma unroll
-                    for (int e = 0; e < V; ++e) acc[e] += wt[i][e] * win[i][e];
-                } else if (hist && active) {
-                    const T *h = hist + ((int64_t)n * (W - 1) + (p - bos + (W - 1))) * C + c0;
-                    const VT hv = *reinterpret_cast<const VT *>(h);
-#pragma unroll
-                    for (int e = 0; e < V; ++e) acc[e] += wt[i][e] * (A)to_f32(hv[e]);
-                }
+        for (int i = 0; i < W; ++i) {
+            const int64_t p = t - (W - 1) + i;
+            VT r = VT{};
+            if (active) {
+                if (p >= bos)
+                    r = *reinterpret_cast<const VT *>(x + p * C + c0);
+                else if (hist)
+                    r = *reinterpret_cast<const VT *>(
+                        hist + ((int64_t)n * (W - 1) + (p - bos + (W - 1))) * C + c0);
             }
+#pragma unroll
+            for (int e = 0; e < V; ++e) acc[e] += wt[i][e] * (A)to_f32(r[e]);
         }
         VT out;
-        if constexpr (std::is_same<T, bf16>::value) {
-            // Fast path: sigmoid_fast, an fp64 sum of squares and rsqrt_fast.  Each
-            // y carries at most 1.8 u relative error from its sigmoid, the norm at
-            // most the largest of those over the head, so the fp32 rounding of the
-            // result lies within 2 * 1.8 u * 2^24 + 1/2 < 4.2 fp32 ulps of the exact
-            // value and rounds to the correctly rounded bf16 whenever
-            // bf16_rounding_sure says so.  Otherwise (about 1 token in 20 per wave)
-            // the wave redoes the token in fp64.
-            A yv[V];
-            bool unsure = false;
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-                yv[e] = silu ? acc[e] * sigmoid_fast(acc[e]) : acc[e];
-                unsure |= silu && acc[e] < -80.0;
-            }
-            if constexpr (LPG > 0) {
-                A ss = 0;
-#pragma unroll
-                for (int e = 0; e < V; ++e) ss += yv[e] * yv[e];
-                const double s = group_sum<LPG>(ss) + (double)eps;
-                unsure |= !(s >= 0x1p-100 && s <= 0x1p100);
-                const double inv = rsqrt_fast(s);
-#pragma unroll
-                for (int e = 0; e < V; ++e) yv[e] *= inv;
-            }
-            float yf[V];
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-                yf[e] = (float)yv[e];
-                unsure |= !bf16_rounding_sure(yf[e]);
-            }
-            if (__builtin_amdgcn_ballot_w64(unsure && active) != 0) {
-                if (silu) {
-#pragma unroll
-                    for (int e = 0; e < V; ++e) acc[e] = silu_of(acc[e]);
-                }
-                if constexpr (LPG > 0) {
-                    A ss = 0;
-#pragma unroll
-                    for (int e = 0; e < V; ++e) ss += acc[e] * acc[e];
-                    ss = group_sum<LPG>(ss);
-                    const A inv = inv_norm(ss, eps);
-#pragma unroll
-                    for (int e = 0; e < V; ++e) acc[e] *= inv;
-                }
-#pragma unroll
-                for (int e = 0; e < V; ++e) out[e] = bf16_from_f64(acc[e]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < V; ++e) out[e] = (bf16)yf[e];
-            }
+        if constexpr (kBf16) {
+            if (__builtin_amdgcn_ballot_w64(finish_fast<LPG>(acc, silu, eps, out) && active) != 0)
+                finish_exact<LPG>(acc, silu, eps, out);
         } else {
-            if (silu) {
-#pragma unroll
-                for (int e = 0; e < V; ++e) acc[e] = silu_of(acc[e]);
-            }
-            if constexpr (LPG > 0) {
-                A ss = 0;
-#pragma unroll
-                for (int e = 0; e < V; ++e) ss += acc[e] * acc[e];
-                ss = group_sum<LPG>(ss);
-                const A inv = inv_norm(ss, eps);
-#pragma unroll
-                for (int e = 0; e < V; ++e) acc[e] *= inv;
-            }
-#pragma unroll
-            for (int e = 0; e < V; ++e) out[e] = acc[e];
+            finish_plain<LPG>(acc, silu, eps, out);
         }
         if (active) *reinterpret_cast<VT *>(y + t * C + c0) = out;
     }
@@ -351,7 +444,14 @@ hipError_t launch_conv(const ConvArgs &a, hipStream_t s) {
         const int64_t nvec = C / ConvVec<T>::n;
         dim3 grid((unsigned)((nvec + kConvThreads - 1) / kConvThreads),
                   (unsigned)((a.total_tokens + kConvTile - 1) / kConvTile));
-        hipLaunchKernelGGL((conv_kernel<T, W, LPG>), grid, dim3(kConvThreads), 0, s,
+        // bf16: the activation is a template switch (it sits inside the straight-line
+        // interior tile); fp32 takes the run-time flag.
+        decltype(&conv_kernel<T, W, LPG, -1>) kernel;
+        if constexpr (std::is_same<T, bf16>::value)
+            kernel = a.silu ? conv_kernel<T, W, LPG, 1> : conv_kernel<T, W, LPG, 0>;
+        else
+            kernel = conv_kernel<T, W, LPG, -1>;
+        hipLaunchKernelGGL(kernel, grid, dim3(kConvThreads), 0, s,
                            (const T *)a.x, (const T *)a.weight, (const T *)a.bias, a.cu_seqlens,
                            a.num_seqs, a.total_tokens, C, (const T *)a.state_in, a.silu, a.eps,
                            (T *)a.y);
