@@ -69,12 +69,15 @@ __device__ __forceinline__ void split_pair(float x0, float x1, bf16x2 &hi, bf16x
     bf16x2 h;
     h[0] = (bf16)x0;
     h[1] = (bf16)x1;
-    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+    uint32_t hb = __builtin_bit_cast(uint32_t, h);
+    // (opaque to the optimiser, which would otherwise convert x0 a second time
+    // to rebuild h0 instead of shifting the packed pair)
+    asm("" : "+v"(hb));
     const float h0 = __uint_as_float(hb << 16), h1 = __uint_as_float(hb & 0xffff0000u);
     bf16x2 l;
     l[0] = (bf16)(x0 - h0);
     l[1] = (bf16)(x1 - h1);
-    hi = h;
+    hi = __builtin_bit_cast(bf16x2, hb);
     lo = l;
 }
 

@@ -59,7 +59,8 @@ hipError_t run(const ChunkArgs &a, hipStream_t s) {
         const int units = a.num_seqs * a.heads;
         const int nslice = a.dv / BV;
         const unsigned g2 = (unsigned)(((units + 7) / 8) * 8 * nslice);
-        hipLaunchKernelGGL((chunk_state_kernel<T, TO, DK, BV, C>), dim3(g2), dim3(512), 0, s,
+        hipLaunchKernelGGL((chunk_state_kernel<T, TO, DK, BV, C>), dim3(g2),
+                           dim3(StateCfg<T, DK, BV, C>::NT), 0, s,
                            (const T *)a.q, (const T *)a.k, (const T *)a.v, a.g, tb, pm,
                            a.cu_seqlens, a.total_tokens, a.heads, a.dv, a.scale, a.h0, a.hT,
                            (TO *)a.o, units, nslice);

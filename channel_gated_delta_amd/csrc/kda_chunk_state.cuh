@@ -23,6 +23,10 @@
 
 #include "kda_chunk_common.cuh"
 
+#ifndef KDA_STATE_NPW
+#define KDA_STATE_NPW 4
+#endif
+
 namespace kda {
 
 template <class T, int DK_, int BV_, int C_>
@@ -30,7 +34,10 @@ struct StateCfg {
     static constexpr int DK = DK_, BV = BV_, C = C_;
     static constexpr bool kSplit = std::is_same<T, bf16>::value;
     static constexpr int NSPLIT = kSplit ? 2 : 1;
-    static constexpr int NT = 512, NPW = 4;                     // threads, producer waves
+    // producer waves (KDA_STATE_NPW for dk >= 64 and 16-token chunks), threads: 4
+    // consumer waves + producers
+    static constexpr int NPW = (DK >= 64 && C == 16) ? KDA_STATE_NPW : 4;
+    static constexpr int NT = (4 + NPW) * kWave;
     static constexpr int NTC = C / 16, NTK = DK / 16, NCW = BV / 16;
     static constexpr int PAD = 16 / (int)sizeof(T);
     static constexpr int LDK = DK + PAD;                        // [C][DK] operand rows
@@ -41,8 +48,10 @@ struct StateCfg {
     static constexpr int RG = (kWave / CPW) < C ? (kWave / CPW) : C;
     static constexpr int RP = C / RG;
     static constexpr int NPT = NPW * kWave;                     // producer threads
-    static constexpr int NTB = C * C / NPT;                     // Tb / P elements per thread
-    static constexpr int NVE = C * BV / NPT;                    // V elements per thread
+    // Tb / P and V elements per thread; with more producer threads than elements
+    // only the first C*C (C*BV) / NTB (NVE) threads take part
+    static constexpr int NTB = C * C / NPT > 0 ? C * C / NPT : 1;
+    static constexpr int NVE = C * BV / NPT > 0 ? C * BV / NPT : 1;
     static_assert(CPW >= 1 && RG * RP == C && NCW <= 4 && BV % 16 == 0, "shape");
     static_assert(NTB >= 1 && (NTB == 1 || NTB % 4 == 0) && NVE >= 1, "shape");
 
@@ -232,7 +241,7 @@ __device__ __forceinline__ void state_chain_bf16(
 }
 
 template <class T, class TO, int DK, int BV, int C>
-__global__ __launch_bounds__(512, 1)
+__global__ __launch_bounds__((StateCfg<T, DK, BV, C>::NT), 1)
 void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                         const float *__restrict__ g, const float *__restrict__ tb,
                         const float *__restrict__ pm, const int32_t *__restrict__ cu_seqlens,
@@ -276,6 +285,7 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
         const bool act = rg < RG;
         const int tr = (pt * NTB) / C, tc = (pt * NTB) % C;   // Tb / P: row tr, cols tc..
         const int vr = (pt * NVE) / BV, vcol = (pt * NVE) % BV;  // V: row vr, cols vcol..
+        const bool tb_act = tr < C, v_act = vr < C;           // (rows >= C: no part)
 
         // Two register sets for the prefetched inputs, used alternately: the loads
         // for chunk s+1 never target registers still holding chunk s, so no copy
@@ -377,7 +387,7 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
             T *sPh = reinterpret_cast<T *>(st + Cfg::oP), *sPl = sPh + (SPLIT ? CCE : 0);
             float *sV = reinterpret_cast<float *>(st + Cfg::oV);
             float *sEGn = reinterpret_cast<float *>(st + Cfg::oEGn);
-            {
+            if (tb_act) {
                 const int i = tr * LDC + tc;
                 if constexpr (NTB == 1) {
                     put1(sTbh, sTbl, i, tbv[0]);
@@ -389,6 +399,8 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                         put2(sPh, sPl, i + e, pmv[e], pmv[e + 1]);
                     }
                 }
+            }
+            if (v_act) {
 #pragma unroll
                 for (int e = 0; e < NVE; ++e) sV[vr * LDV + vcol + e] = vv[e];
             }
