@@ -39,7 +39,11 @@ struct StateCfg {
     static constexpr int NPW = (DK >= 64 && C == 16) ? KDA_STATE_NPW : 4;
     static constexpr int NT = (4 + NPW) * kWave;
     static constexpr int NTC = C / 16, NTK = DK / 16, NCW = BV / 16;
-    static constexpr int PAD = 16 / (int)sizeof(T);
+    // Row pitch padding (elements).  For bf16 the pitches come out at 2 (mod 32)
+    // dwords, so the 16 rows one LDS cycle serves fall in 16 different bank pairs
+    // (an 8-element pad would map rows r and r + 8 to the same banks); fragments are
+    // 8-byte loads, so 8-byte row alignment suffices.
+    static constexpr int PAD = 4;
     static constexpr int LDK = DK + PAD;                        // [C][DK] operand rows
     static constexpr int LDC = C + PAD;                         // [*][C] operand rows
     static constexpr int LDV = BV + 4;                          // fp32 [C][BV] rows
