@@ -81,6 +81,30 @@ __device__ __forceinline__ void split_pair(float x0, float x1, bf16x2 &hi, bf16x
     lo = l;
 }
 
+// Eight floats split into 16x16x32 operand tuples hi, lo (x = hi + lo), with the
+// packed high parts kept as one register tuple (no copies into the operand).
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    u4 hb, lb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf16x2 h;
+        h[0] = (bf16)x[2 * e];
+        h[1] = (bf16)x[2 * e + 1];
+        hb[e] = __builtin_bit_cast(uint32_t, h);
+    }
+    asm("" : "+v"(hb));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf16x2 l;
+        l[0] = (bf16)(x[2 * e] - __uint_as_float(hb[e] << 16));
+        l[1] = (bf16)(x[2 * e + 1] - __uint_as_float(hb[e] & 0xffff0000u));
+        lb[e] = __builtin_bit_cast(uint32_t, l);
+    }
+    hi = __builtin_bit_cast(bf16x8, hb);
+    lo = __builtin_bit_cast(bf16x8, lb);
+}
+
 // Store x0, x1 at H[i], H[i+1] (and the low parts at L[i], L[i+1] when T is bf16).
 template <class T>
 __device__ __forceinline__ void put2(T *H, T *L, int i, float x0, float x1) {

@@ -48,10 +48,20 @@ hipError_t run(const ChunkArgs &a, hipStream_t s) {
         float *tb = a.workspace;
         float *pm = tb ? tb + (size_t)a.total_tokens * a.heads * C : nullptr;
         if (a.total_tokens > 0) {
-            const dim3 g1((unsigned)((a.total_tokens + C - 1) / C), (unsigned)a.heads);
-            hipLaunchKernelGGL((chunk_prep_kernel<T, DK, C>), g1, dim3(256), 0, s,
-                               (const T *)a.q, (const T *)a.k, a.g, a.beta, a.cu_seqlens,
-                               a.num_seqs, a.total_tokens, a.heads, a.scale, tb, pm);
+            const int64_t ntiles = (a.total_tokens + C - 1) / C;
+            if constexpr (std::is_same<T, bf16>::value && C == 16 && DK % 32 == 0) {
+                // one wave per (tile, head), four per workgroup
+                const int64_t units = ntiles * a.heads;
+                hipLaunchKernelGGL((chunk_prep16_kernel<DK>), dim3((unsigned)((units + 3) / 4)),
+                                   dim3(256), 0, s, (const bf16 *)a.q, (const bf16 *)a.k, a.g,
+                                   a.beta, a.cu_seqlens, a.num_seqs, a.total_tokens, a.heads,
+                                   a.scale, units, tb, pm);
+            } else {
+                const dim3 g1((unsigned)ntiles, (unsigned)a.heads);
+                hipLaunchKernelGGL((chunk_prep_kernel<T, DK, C>), g1, dim3(256), 0, s,
+                                   (const T *)a.q, (const T *)a.k, a.g, a.beta, a.cu_seqlens,
+                                   a.num_seqs, a.total_tokens, a.heads, a.scale, tb, pm);
+            }
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

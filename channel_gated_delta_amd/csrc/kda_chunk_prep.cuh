@@ -326,4 +326,170 @@ void chunk_prep_kernel(const T *__restrict__ q, const T *__restrict__ k,
     }
 }
 
+// ---------------------------------------------------------------------------
+// One wave per (16-token tile, head): the bf16, 16-token form of the prep kernel.
+//
+// Lane l holds row t = l & 15 of the chunk and, for key block j, channels
+// 32j + 8(l >> 4) .. +7 -- exactly the A / B fragment layout of the 16x16x32
+// product -- so the Gram operands are built and split in registers and go
+// straight into the MFMA (M = X Y^T when both operands are row fragments).  The
+// in-chunk log2-decay prefix runs over the 16 rows of a DPP row (row_shr steps),
+// the middle-row reference comes from lane 8 of the row, and the exact diagonal
+// of P is a 4-lane sum.  Only the 16 x 16 forward substitution goes through a
+// small wave-private LDS tile; there is no workgroup barrier.
+// ---------------------------------------------------------------------------
+#ifndef KDA_PREP16_MINB
+#define KDA_PREP16_MINB 3
+#endif
+template <int S>
+__device__ __forceinline__ float row_shr_zero(float v) {   // lane l%16 >= S: lane l-S, else 0
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + S, 0xf, 0xf, false));
+}
+
+template <int DK>
+__global__ __launch_bounds__(256, KDA_PREP16_MINB)
+void chunk_prep16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+                         const float *__restrict__ g, const float *__restrict__ beta,
+                         const int32_t *__restrict__ cu_seqlens, int nseq, int64_t total, int H,
+                         float scale, int64_t units, float *__restrict__ tb_out,
+                         float *__restrict__ p_out) {
+    constexpr int C = 16, NKB = DK / 32, LDA = C + 4;   // 16-byte aligned tile rows
+    static_assert(DK % 32 == 0, "shape");
+    __shared__ __attribute__((aligned(16))) float smem[4][2 * C * LDA + C];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + wave;
+    if (unit >= units) return;                 // the whole wave: no workgroup barriers below
+    float *sA = smem[wave], *sP = sA + C * LDA, *sB = sP + C * LDA;
+    const int h = (int)(unit % H);             // heads fastest: a workgroup shares its rows
+    const int64_t t0 = (unit / H) * C, t1 = min(t0 + C, total);
+    const size_t rowQK = (size_t)H * DK;
+    const int t = lane & 15, kb = lane >> 4;
+
+    int n = 0;
+    if (cu_seqlens) {
+        int lo = 0, hi = nseq - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (chunk_seq_off(cu_seqlens, mid, total) <= t0) lo = mid; else hi = mid - 1;
+        }
+        n = lo;
+    }
+    for (; n < nseq; ++n) {
+        const int64_t bos = chunk_seq_off(cu_seqlens, n, total);
+        if (bos >= t1) break;
+        const int64_t eos = max(chunk_seq_off(cu_seqlens, n + 1, total), bos);
+        const int64_t cs = bos >= t0 ? bos : bos + ((t0 - bos + C - 1) / C) * C;
+        if (cs >= t1 || cs >= eos) continue;
+        const int nt = __builtin_amdgcn_readfirstlane((int)min((int64_t)C, eos - cs));
+        // Rows >= nt read copies of the last row and are left unmasked: no row < nt
+        // depends on them (the prefix runs forward, the substitution reads A[r][m]
+        // with m < r, P is lower triangular) and they are never written; the middle-
+        // row reference stays within 8 rows of decay of every row either way.
+        const size_t off = (size_t)(cs + min(t, nt - 1)) * rowQK + (size_t)h * DK + 8 * kb;
+        f32x4 A3[3], P3[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) A3[i] = P3[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float dg = 0.f;                        // this lane's part of q_t . k_t
+#pragma unroll
+        for (int j = 0; j < NKB; ++j) {
+            const bf16x8 qr = *reinterpret_cast<const bf16x8 *>(q + off + 32 * j);
+            const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(k + off + 32 * j);
+            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(g + off + 32 * j);
+            const f32x4 g1 = *reinterpret_cast<const f32x4 *>(g + off + 32 * j + 4);
+            float x[8], qd[8], kd[8], kc[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (e < 4 ? g0[e] : g1[e - 4]) * kLog2e;
+            // inclusive prefix over the rows (G_t, log2 units)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                x[e] += row_shr_zero<1>(x[e]);
+                x[e] += row_shr_zero<2>(x[e]);
+                x[e] += row_shr_zero<4>(x[e]);
+                x[e] += row_shr_zero<8>(x[e]);
+            }
+            // the middle row's G (lane 8 of each row), all eight requests in flight
+            float gm[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gm[e] = __shfl(x[e], (lane & ~15) | 8, kWave);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // referenced at the middle row: |d| <= 8 |lb| log2 e <= 104 for gates
+                // down to -9, so both factors are finite normal numbers
+                const float d = x[e] - gm[e];
+                const float dr = __builtin_amdgcn_exp2f(d), dc = __builtin_amdgcn_exp2f(-d);
+                const float qv = (float)qr[e], kv = (float)kr[e];
+                dg += qv * kv;
+                qd[e] = qv * dr;
+                kd[e] = kv * dr;
+                kc[e] = kv * dc;
+            }
+            bf16x8 QH, QL, KH, KL, CH, CL;
+            split8(qd, QH, QL);
+            split8(kd, KH, KL);
+            split8(kc, CH, CL);
+            // A = Kd Kc^T, P = Qd Kc^T (hi*hi + hi*lo + lo*hi, one accumulator per term)
+            A3[0] = mma(KH, CH, A3[0]);
+            P3[0] = mma(QH, CH, P3[0]);
+            A3[1] = mma(KH, CL, A3[1]);
+            P3[1] = mma(QH, CL, P3[1]);
+            A3[2] = mma(KL, CH, A3[2]);
+            P3[2] = mma(QL, CH, P3[2]);
+        }
+        // q_t . k_t over the four lanes of row t (one per 16-lane row of the wave)
+        dg = halves_sum(rowpair_sum(dg));
+
+        // A (strictly lower) and scale * P (lower, exact diagonal) into the wave's tiles
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = acc_row(lane, r), col = acc_col(lane);
+            const float a = A3[0][r] + (A3[1][r] + A3[2][r]);
+            const float p = P3[0][r] + (P3[1][r] + P3[2][r]);
+            sA[row * LDA + col] = row > col ? a : 0.f;
+            // the exact diagonal: lane col holds row col's dot product
+            sP[row * LDA + col] = row > col ? scale * p : (row == col ? scale * dg : 0.f);
+        }
+        if (lane < C) sB[lane] = lane < nt ? beta[(size_t)(cs + lane) * H + h] : 0.f;
+        // wave-private tiles: the LDS ops of one wave complete in order
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+
+        // Tb = (I + diag(beta) A)^{-1} diag(beta): lane i builds column i by forward
+        // substitution (rows above i come out zero by themselves: every term of their
+        // sums is), scales it by beta_i and writes it over the A tile, which no lane
+        // reads any more once the substitution is done.
+        if (lane < C) {
+            const int i = lane;
+            float xs[C];
+#pragma unroll
+            for (int r = 0; r < C; ++r) {
+                float sum = 0.f;
+#pragma unroll
+                for (int m = 0; m < r; ++m) sum = fmaf(sA[r * LDA + m], xs[m], sum);
+                const float v = -sB[r] * sum;
+                xs[r] = r == i ? 1.f : v;
+            }
+            const float bi = sB[i];
+#pragma unroll
+            for (int r = 0; r < C; ++r) sA[r * LDA + i] = xs[r] * bi;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+        // rows of Tb and P: lane l writes columns 4 (l & 3) .. +3 of row l >> 2
+        {
+            const int rr = lane >> 2, cc = 4 * (lane & 3);
+            if (rr < nt) {
+                const size_t o = ((size_t)(cs + rr) * H + h) * C + cc;
+                *reinterpret_cast<f32x4 *>(tb_out + o) = *reinterpret_cast<const f32x4 *>(sA + rr * LDA + cc);
+                *reinterpret_cast<f32x4 *>(p_out + o) = *reinterpret_cast<const f32x4 *>(sP + rr * LDA + cc);
+            }
+        }
+        // the next chunk of this tile reuses the tile only after every lane's reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    }
+}
+
 }  // namespace kda
