@@ -130,7 +130,6 @@ __device__ __forceinline__ void state_chain_bf16(
         fk[0][R] = lda8(sKdh, sKdl, LDK, R * 16, 0, lane);
         fq[0][R] = lda8(sQdh, sQdl, LDK, R * 16, 0, lane);
     }
-    // sb holds the state as B operand (hi, lo), split at the end of the previous step
 
     // E = Kd S, O = Qd S: k-block j's products while block j+1 loads.  The three
     // split terms go to separate accumulators (summed at the end), so 6 NTC
@@ -143,6 +142,9 @@ __device__ __forceinline__ void state_chain_bf16(
             Et3[t][R] = f32x4{0.f, 0.f, 0.f, 0.f};
             Ot3[t][R] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+    // The state is split into (hi, lo) B operands here, block by block: block j+1's
+    // split runs beside block j's products instead of after the previous update.
+    sb[0] = breg8(Sacc[0], Sacc[1]);
 #pragma unroll
     for (int j = 0; j < NKB; ++j) {
         const int cur = j & 1, nxt = cur ^ 1;
@@ -154,6 +156,7 @@ __device__ __forceinline__ void state_chain_bf16(
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (j + 1 < NKB) sb[j + 1] = breg8(Sacc[2 * j + 2], Sacc[2 * j + 3]);
         // term-major order: the 2*NTC accumulators interleave, so no product waits
         // for the one before it
 #pragma unroll
@@ -239,9 +242,6 @@ __device__ __forceinline__ void state_chain_bf16(
 #pragma unroll
         for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr4[rt].l, ub4.h, Sacc[rt]);
     }
-    // split the new state for the next step now: it overlaps the step barrier
-#pragma unroll
-    for (int j = 0; j < NKB; ++j) sb[j] = breg8(Sacc[2 * j], Sacc[2 * j + 1]);
 }
 
 template <class T, class TO, int DK, int BV, int C>
