@@ -252,7 +252,7 @@ def main():
     traffic = measured_traffic("chunk", args.workload)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "kda_chunk_fwd (chunk_prep_kernel + chunk_state_kernel)",
+            "kernel": "kda_chunk_fwd (chunk_prep16_kernel + chunk_state_kernel)",
             "algorithmic_bytes_per_launch": alg_bytes,
             "avg_launch_ms": round(res["chunk_ms"], 4)}
     out = {
