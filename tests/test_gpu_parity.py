@@ -245,7 +245,7 @@ def decode_case(B, H, dk, dv, steps, dtype, seed, pairs=None):
     return state
 
 
-@pytest.mark.parametrize("dk,dv", [(128, 128), (16, 16), (32, 128), (128, 16), (64, 64)])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (16, 16), (32, 128), (128, 16), (64, 64), (16, 32)])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
 def test_decode_small(dk, dv, dtype):
     note("decode dk=%d dv=%d %s" % (dk, dv, dtype))
