@@ -486,13 +486,14 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                     Sacc[rt][r] = src[(size_t)(rt * 16 + acc_row(lane, r)) * DV + vc];
             }
         }
-        // the state split into (hi, lo) B operands, refreshed at the end of each chain
+        // Wait for the h0 loads here, once.  The memory counter also counts this
+        // wave's output stores, and a load still pending into the state registers
+        // at the loop entry would make the compiler wait for the counter inside the
+        // loop -- for the previous step's stores to complete, at every step.
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt untouched
+        // (hi, lo) B operands of the state, built block by block inside each chain
         constexpr int NKB = DK / 32 > 0 ? DK / 32 : 1;
         BReg8 sbs[NKB];
-        if constexpr (SPLIT && DK % 32 == 0) {
-#pragma unroll
-            for (int j = 0; j < NKB; ++j) sbs[j] = breg8(Sacc[2 * j], Sacc[2 * j + 1]);
-        }
         for (int s = 0; s < nsteps; ++s) {
             if (s >= 1 && s <= nchunks && owner) {
                 const int64_t c0 = bos + (int64_t)(s - 1) * C;
