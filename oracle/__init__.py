@@ -22,6 +22,7 @@ Sources are web pages, cited by title and section:
 
 Contents:
 
+* ``bounded_gate`` (O0) log-decay from the bounded gate's pre-activation -- C, fp64
 * ``short_conv``  (O1a) causal depthwise conv + SiLU with conv cache  -- C, fp64
 * ``l2norm``      (O1b) q/k L2 normalisation                          -- C, fp64
 * ``round_bf16``  (O1c) rounding of an interface tensor to bf16         -- C, fp64
@@ -98,6 +99,9 @@ class OracleLib:
         lib.kda_oracle_recurrent.restype = ctypes.c_int
         lib.kda_oracle_round_bf16.argtypes = [_dp, ctypes.c_int64]
         lib.kda_oracle_round_bf16.restype = None
+        lib.kda_oracle_bounded_gate.argtypes = [
+            _dp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _dp, _dp, ctypes.c_double, _dp]
+        lib.kda_oracle_bounded_gate.restype = None
         lib.kda_oracle_num_threads.argtypes = []
         lib.kda_oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -105,6 +109,21 @@ class OracleLib:
 
     def num_threads(self) -> int:
         return int(self.lib.kda_oracle_num_threads())
+
+    def bounded_gate(self, z, a_log=None, dt_bias=None, lower_bound: float = -5.0):
+        """O0: g = lower_bound * sigmoid(exp(A_log[h]) * (z + dt_bias[h, c])).
+
+        z: [T, H, D]; a_log: [H] or None (0); dt_bias: [H, D] or None (0).
+        Returns g [T, H, D], the log-decay (lower_bound <= g <= 0).
+        """
+        z = _f64(z)
+        T, H, D = z.shape
+        al = None if a_log is None else _f64(a_log).reshape(H)
+        dt = None if dt_bias is None else _f64(dt_bias).reshape(H, D)
+        g = np.empty((T, H, D))
+        self.lib.kda_oracle_bounded_gate(_ptr(z), T, H, D, _ptr(al), _ptr(dt),
+                                         float(lower_bound), _ptr(g))
+        return g
 
     def short_conv(self, x, w, cu_seqlens=None, state_in=None, bias=None, silu=True,
                    return_state=False):
@@ -201,6 +220,10 @@ def default() -> OracleLib:
 
 def num_threads() -> int:
     return default().num_threads()
+
+
+def bounded_gate(*a, **kw):
+    return default().bounded_gate(*a, **kw)
 
 
 def short_conv(*a, **kw):

@@ -92,6 +92,28 @@ int kda_oracle_short_conv(const double *x, int64_t total_tokens, int64_t C,
 }
 
 /*
+ * O0. Bounded forget gate ([Walkthrough] 彩蛋: the gate function with a lower
+ *     bound).  From the gate's pre-activation z, a learnable per-head parameter
+ *     A_log[h] and a per-channel bias dt_bias[h, c], the log-decay is
+ *         g = lower_bound * sigmoid(exp(A_log[h]) * (z + dt_bias[h, c])),
+ *     sigmoid(y) = 1 / (1 + e^-y), so lower_bound <= g <= 0 and the retention
+ *     alpha = e^g lies in [e^lower_bound, 1] (lower_bound = -5 in K3).
+ * z, g: [T, H, D]; a_log: [H] or NULL (0); dt_bias: [H, D] or NULL (0).
+ */
+void kda_oracle_bounded_gate(const double *z, int64_t T, int H, int D, const double *a_log,
+                             const double *dt_bias, double lower_bound, double *g) {
+    for (int64_t t = 0; t < T; ++t)
+        for (int h = 0; h < H; ++h) {
+            const double a = exp(a_log ? a_log[h] : 0.0);
+            for (int c = 0; c < D; ++c) {
+                const int64_t i = (t * H + h) * D + c;
+                const double y = a * (z[i] + (dt_bias ? dt_bias[(int64_t)h * D + c] : 0.0));
+                g[i] = lower_bound / (1.0 + exp(-y));
+            }
+        }
+}
+
+/*
  * O1b. L2 normalisation of q and k ([Walkthrough] 第二站: after conv+SiLU the
  *      query and key are scaled to (close to) unit length; the operator does it).
  * x: [rows, D], each row scaled in place by 1 / sqrt(sum_c x_c^2 + eps).

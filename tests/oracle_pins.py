@@ -350,9 +350,42 @@ def pin_k3_sizes(orc=None):
     assert gd["subchunk_tokens"] * gd["gate_lower_bound"] == lo and hi == 0.0
 
 
+def pin_bounded_gate(orc):
+    """Walkthrough 彩蛋: g = lb * sigmoid(e^{A_log[h]} (z + dt_bias[h, c])).
+
+    sigmoid(0) = 1/2 and sigmoid(ln 3) = 3/4 give closed forms; A_log enters
+    through its exponential (per head), dt_bias is added per (head, channel),
+    and lb <= g <= 0 with g decreasing in z.
+    """
+    T, H, D = 3, 2, 4
+    ln3 = np.log(3.0)
+    for lb in (-5.0, -8.0):
+        # no A_log, no bias: rows z = 0, ln 3, -ln 3
+        z = np.zeros((T, H, D))
+        z[1], z[2] = ln3, -ln3
+        g = orc.bounded_gate(z, lower_bound=lb)
+        for t, f in enumerate((0.5, 0.75, 0.25)):
+            _close(g[t], np.full((H, D), f * lb), 1e-15, "gate closed form row %d" % t)
+        # A_log = ln 2 doubles the argument of head 1 only
+        z = np.full((T, H, D), ln3 / 2)
+        g = orc.bounded_gate(z, a_log=np.array([0.0, np.log(2.0)]), lower_bound=lb)
+        _close(g[:, 1], np.full((T, D), 0.75 * lb), 1e-15, "gate A_log head 1")
+        _close(g[:, 0], np.full((T, D), lb / (1.0 + 3.0 ** -0.5)), 1e-15, "gate A_log head 0")
+        # the per-channel bias shifts z: z = ln 3 - dt gives 3/4 everywhere
+        dt = 0.1 * np.arange(1, H * D + 1).reshape(H, D)
+        g = orc.bounded_gate(np.broadcast_to(ln3 - dt, (T, H, D)), dt_bias=dt, lower_bound=lb)
+        _close(g, np.full((T, H, D), 0.75 * lb), 1e-14, "gate dt_bias")
+    # bounds and monotonicity on random pre-activations
+    rng = np.random.default_rng(21)
+    z = np.sort(rng.normal(0.0, 4.0, (64, 1, 1)), axis=0)
+    g = orc.bounded_gate(z, a_log=np.array([0.3]), dt_bias=np.array([[0.2]]), lower_bound=-5.0)
+    assert np.all(g >= -5.0) and np.all(g <= 0.0), "gate outside [lb, 0]"
+    assert np.all(np.diff(g[:, 0, 0]) <= 0.0), "gate not decreasing in z"
+
+
 ALL_PINS = [
     pin_unit_key_example, pin_one_dim_example, pin_two_address_example, pin_update_order,
     pin_identity, pin_pure_decay, pin_overwrite, pin_linear_attention, pin_gated_form,
     pin_chunked_matches_recurrent, pin_causality, pin_conv_library, pin_l2norm, pin_round_bf16,
-    pin_varlen_and_resume, pin_value_columns_independent, pin_k3_sizes,
+    pin_varlen_and_resume, pin_value_columns_independent, pin_k3_sizes, pin_bounded_gate,
 ]

@@ -53,6 +53,13 @@ MUTANTS = {
     "bias_dropped": [("double acc = bias ? bias[c] : 0.0;", "double acc = 0.0;")],
     "bf16_truncates": [("x[i] = ldexp(nearbyint(ldexp(m, 8)), e - 8);", "x[i] = ldexp(trunc(ldexp(m, 8)), e - 8);")],
     "bf16_round_half_up": [("x[i] = ldexp(nearbyint(ldexp(m, 8)), e - 8);", "x[i] = ldexp(round(ldexp(m, 8)), e - 8);")],
+    "gate_alog_not_exponentiated": [("const double a = exp(a_log ? a_log[h] : 0.0);",
+                                     "const double a = a_log ? a_log[h] : 1.0;")],
+    "gate_bias_multiplied": [("(z[i] + (dt_bias ? dt_bias[(int64_t)h * D + c] : 0.0))",
+                              "(z[i] * (dt_bias ? dt_bias[(int64_t)h * D + c] : 1.0))")],
+    "gate_bias_per_head": [("dt_bias[(int64_t)h * D + c]", "dt_bias[h]")],
+    "gate_sigmoid_sign": [("g[i] = lower_bound / (1.0 + exp(-y));", "g[i] = lower_bound / (1.0 + exp(y));")],
+    "gate_bound_dropped": [("g[i] = lower_bound / (1.0 + exp(-y));", "g[i] = -1.0 / (1.0 + exp(-y));")],
 }
 
 
