@@ -14,6 +14,9 @@ written).  ``value`` is prefill tokens/s.  The same JSON line carries:
   kernel source, else null;
 * ``decode``: 256 in-place decode steps of 64 sequences x 96 heads (steps/s) and
   the decode kernel's roofline;
+* ``fused_gate``: the same prefill step with the bounded gate formed inside the
+  chunk kernels from bf16 pre-activations (kda_chunk_fwd_gated) instead of a
+  precomputed fp32 g, and that call's roofline;
 * ``cpu_baseline``: the fp64 oracle (prologue + recurrence) timed on this host's
   cores over the same workload, repeated for at least ten seconds.
 
@@ -40,6 +43,8 @@ KERNEL_SOURCES = {
     "chunk": ("kda_device.cuh", "kda_chunk_common.cuh", "kda_chunk_prep.cuh", "kda_chunk_state.cuh",
               "kda_chunk_dispatch.cuh", "kda_chunk_bf16.hip"),
     "decode": ("kda_device.cuh", "kda_decode.hip"),
+    "gated": ("kda_device.cuh", "kda_chunk_common.cuh", "kda_chunk_prep.cuh",
+              "kda_chunk_state.cuh", "kda_chunk_dispatch.cuh", "kda_chunk_bf16_gz.hip"),
 }
 
 
@@ -78,6 +83,12 @@ def prefill_step_bytes(T: int, H: int, dk: int, dv: int, N: int, h0: bool) -> fl
     return float(T * H * per_tok_head + states)
 
 
+def gated_step_bytes(T: int, H: int, dk: int, dv: int, N: int, h0: bool) -> float:
+    """As prefill_step_bytes with the gate's bf16 pre-activation z (2*dk per token and
+    head) in place of the fp32 g; A_log and dt_bias are negligible."""
+    return prefill_step_bytes(T, H, dk, dv, N, h0) - float(T * H * 2 * dk)
+
+
 def prologue_bytes(T: int, H: int, d: int) -> float:
     """conv4+SiLU(+L2): read x and write y (bf16) for q, k, v; weights are negligible."""
     return float(3 * T * H * d * 2 * 2)
@@ -88,11 +99,12 @@ def decode_step_bytes(B: int, H: int, dk: int, dv: int) -> float:
     return float(B * H * (2 * dk * dv * 4 + 2 * dk * 2 + dv * 2 + 4 * dk + 4 + 4 * dv))
 
 
-def run_prefill(args, torch, kda, workloads):
+def run_prefill(args, torch, kda, workloads, gated=False):
     specs = workloads.standard_specs()
     spec = specs[args.workload]
     dev = "cuda:0"
     inp = workloads.make_prefill(spec, dev)
+    gate = workloads.make_gate(spec, dev) if gated else None
     H, DK, DV = spec.heads, spec.dk, spec.dv
     T, N = spec.total_tokens, len(spec.lengths)
     cu = inp["cu_seqlens"] if N > 1 else None
@@ -113,9 +125,16 @@ def run_prefill(args, torch, kda, workloads):
         kda.short_conv(inp["v_raw"], inp["w_v"], num_heads=H, head_dim=DV, cu_seqlens=cu, out=vb)
         if ev is not None:
             ev[0].record(stream)
-        kda.chunk_fwd(qb, kb, vb, inp["g"], inp["beta"], cu_seqlens=cu, scale=spec.read_scale,
-                      gate_lower_bound=spec.gate_lb, chunk_size=spec.chunk,
-                      initial_state=inp["h0"], out=ob, final_state=hT, workspace=ws)
+        if gate is None:
+            kda.chunk_fwd(qb, kb, vb, inp["g"], inp["beta"], cu_seqlens=cu,
+                          scale=spec.read_scale, gate_lower_bound=spec.gate_lb,
+                          chunk_size=spec.chunk, initial_state=inp["h0"], out=ob, final_state=hT,
+                          workspace=ws)
+        else:
+            kda.chunk_fwd_gated(qb, kb, vb, gate["z"], inp["beta"], a_log=gate["a_log"],
+                                dt_bias=gate["dt_bias"], lower_bound=spec.gate_lb, cu_seqlens=cu,
+                                scale=spec.read_scale, chunk_size=spec.chunk,
+                                initial_state=inp["h0"], out=ob, final_state=hT, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
 
@@ -224,6 +243,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill", choices=["prefill", "varlen", "long"])
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-gate", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (torch elementwise kernel), the "
@@ -283,6 +303,21 @@ def main():
                                       "frac": round(dach / HBM_PEAK_GBS, 4),
                                       "traffic": measured_traffic("decode", "decode"),
                                       "algorithmic_bytes_per_launch": dbytes}}
+    if not args.no_gate:
+        gres = run_prefill(args, torch, kda, workloads, gated=True)
+        gbytes = gated_step_bytes(T, H, DK, DV, N, spec.h0_std is not None)
+        gach = gbytes / (gres["chunk_ms"] / 1e3) / 1e9
+        out["fused_gate"] = {
+            "value": round(T / (gres["ms_step"] / 1e3), 1), "unit": "tokens/s",
+            "ms_per_step": round(gres["ms_step"], 4),
+            "path": "3x short_conv + chunk_fwd_gated (g = lb sigmoid(e^A_log (z + dt_bias)) "
+                    "in-kernel, z bf16)",
+            "roofline": {"bound": "hbm", "achieved": round(gach, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gach / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("gated", args.workload),
+                         "kernel": "kda_chunk_fwd_gated", "algorithmic_bytes_per_launch": gbytes,
+                         "avg_launch_ms": round(gres["chunk_ms"], 4)}}
+        del gres
     out["prologue_ms_per_step"] = round(res["ms_step"] - res["chunk_ms"], 4)
     out["prologue_bytes_per_step"] = prologue_bytes(T, H, DK)
     if not args.no_cpu:

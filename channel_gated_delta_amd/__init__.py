@@ -7,6 +7,7 @@ fallback: if libkda.so is missing the calls raise.
 
     short_conv(x, weight, ...)              -> (y, conv_state)   conv4 + SiLU (+ L2)
     chunk_fwd(q, k, v, g, beta, ...)        -> (o, final_state)  chunkwise prefill
+    chunk_fwd_gated(q, k, v, z, beta, ...)  -> (o, final_state)  the same, bounded gate fused
     decode_step(q, k, v, g, beta, state)    -> o                 one recurrent step
 
 Build the library with ``python -m channel_gated_delta_amd.build``.
@@ -19,7 +20,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["KdaError", "library", "short_conv", "chunk_fwd", "decode_step", "LIB_PATH"]
+__all__ = ["KdaError", "library", "short_conv", "chunk_fwd", "chunk_fwd_gated", "decode_step",
+           "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -50,12 +52,15 @@ def library() -> ctypes.CDLL:
         lib.kda_chunk_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
                                       _i32, _f32, _f32, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                       _i32, _i32, _vp]
+        lib.kda_chunk_fwd_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32,
+                                            _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
+                                            _vp, ctypes.c_size_t, _i32, _i32, _vp]
         lib.kda_chunk_fwd_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _i32,
                                                      ctypes.POINTER(ctypes.c_size_t)]
         lib.kda_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
                                         _vp, _i32, _i32, _vp]
-        for fn in ("kda_short_conv", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
-                   "kda_decode_step"):
+        for fn in ("kda_short_conv", "kda_chunk_fwd", "kda_chunk_fwd_gated",
+                   "kda_chunk_fwd_workspace_size", "kda_decode_step"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_status_string.restype = ctypes.c_char_p
@@ -156,6 +161,39 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     [N, H, dk, dv] (fp32) if requested.  ``workspace`` (a uint8 GPU tensor of at
     least ``chunk_workspace_bytes(...)`` bytes) is allocated when not given.
     """
+    T, H, dk = q.shape
+    _dev(g, "g", torch.float32, (T, H, dk))
+    return _chunk(q, k, v, g, None, beta, cu_seqlens, scale, gate_lower_bound, chunk_size,
+                  initial_state, output_final_state, out, final_state, out_dtype, workspace)
+
+
+def chunk_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, z: torch.Tensor,
+                    beta: torch.Tensor, *, a_log: Optional[torch.Tensor] = None,
+                    dt_bias: Optional[torch.Tensor] = None, lower_bound: float = -5.0,
+                    cu_seqlens: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                    chunk_size: int = 64, initial_state: Optional[torch.Tensor] = None,
+                    output_final_state: bool = True, out: Optional[torch.Tensor] = None,
+                    final_state: Optional[torch.Tensor] = None,
+                    out_dtype: torch.dtype = torch.float32,
+                    workspace: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA prefill with the bounded gate fused in: the kernels form
+    g = lower_bound * sigmoid(exp(a_log[h]) * (z + dt_bias[h, c])) from z [T, H, dk]
+    (q's dtype), a_log [H] and dt_bias [H, dk] (fp32, optional).  Otherwise as
+    ``chunk_fwd``."""
+    T, H, dk = q.shape
+    _dev(z, "z", q.dtype, (T, H, dk))
+    if a_log is not None:
+        _dev(a_log, "a_log", torch.float32, (H,))
+    if dt_bias is not None:
+        _dev(dt_bias, "dt_bias", torch.float32, (H, dk))
+    return _chunk(q, k, v, None, (z, a_log, dt_bias), beta, cu_seqlens, scale, lower_bound,
+                  chunk_size, initial_state, output_final_state, out, final_state, out_dtype,
+                  workspace)
+
+
+def _chunk(q, k, v, g, gate, beta, cu_seqlens, scale, lower_bound, chunk_size, initial_state,
+           output_final_state, out, final_state, out_dtype, workspace):
     _dev(q, "q")
     dt = q.dtype
     if dt not in _DTYPES:
@@ -164,7 +202,6 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     dv = v.shape[-1]
     _dev(k, "k", dt, (T, H, dk))
     _dev(v, "v", dt, (T, H, dv))
-    _dev(g, "g", torch.float32, (T, H, dk))
     _dev(beta, "beta", torch.float32, (T, H))
     N = _seqs(cu_seqlens, T)
     if initial_state is not None:
@@ -184,10 +221,19 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace", torch.uint8)
-    _check(library().kda_chunk_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,
-        int(chunk_size), sc, float(gate_lower_bound), _ptr(initial_state), _ptr(final_state),
-        _ptr(o), _ptr(workspace), workspace.numel(), _DTYPES[dt], _DTYPES[out_dtype], _stream(q)))
+    if gate is None:
+        _check(library().kda_chunk_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,
+            int(chunk_size), sc, float(lower_bound), _ptr(initial_state), _ptr(final_state),
+            _ptr(o), _ptr(workspace), workspace.numel(), _DTYPES[dt], _DTYPES[out_dtype],
+            _stream(q)))
+    else:
+        z, a_log, dt_bias = gate
+        _check(library().kda_chunk_fwd_gated(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(a_log), _ptr(dt_bias), float(lower_bound),
+            _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv, int(chunk_size), sc,
+            _ptr(initial_state), _ptr(final_state), _ptr(o), _ptr(workspace), workspace.numel(),
+            _DTYPES[dt], _DTYPES[out_dtype], _stream(q)))
     return o, final_state
 
 

@@ -33,7 +33,11 @@ int vec_elems(kda_dtype_t) { return 4; }   // channels per lane of the conv kern
 
 namespace {
 
-kda::ChunkLauncher chunk_launcher(kda_dtype_t dtype, kda_dtype_t out_dtype) {
+kda::ChunkLauncher chunk_launcher(kda_dtype_t dtype, kda_dtype_t out_dtype, bool gated = false) {
+    if (gated)
+        return dtype == KDA_DTYPE_F32       ? kda::launch_chunk_f32_gz
+               : out_dtype == KDA_DTYPE_F32 ? kda::launch_chunk_bf16_f32out_gz
+                                            : kda::launch_chunk_bf16_bf16out_gz;
     return dtype == KDA_DTYPE_F32       ? kda::launch_chunk_f32
            : out_dtype == KDA_DTYPE_F32 ? kda::launch_chunk_bf16_f32out
                                         : kda::launch_chunk_bf16_bf16out;
@@ -74,6 +78,40 @@ int chunk_shape_check(const char *who, int64_t total_tokens, int32_t num_heads, 
     (void)chunk_launcher(dtype, out_dtype)(probe, nullptr, false, &c);
     if (c == 0) *st = fail(KDA_ERR_UNSUPPORTED, "%s: no kernel for dk=%d dv=%d", who, dk, dv);
     return c;
+}
+
+// The checks and the launch shared by kda_chunk_fwd and kda_chunk_fwd_gated;
+// `gate` is g or the gate's pre-activation z.
+kda_status_t chunk_checked_launch(const char *who, const kda::ChunkArgs &a, const void *gate,
+                                  bool gated, size_t workspace_bytes, kda_dtype_t dtype,
+                                  kda_dtype_t out_dtype, void *stream) {
+    if (a.total_tokens > 0 &&
+        (!a.q || !a.k || !a.v || !gate || !a.beta || !a.o || !a.workspace))
+        return fail(KDA_ERR_INVALID_ARG, "%s: NULL q/k/v/%s/beta/o/workspace", who,
+                    gated ? "z" : "g");
+    if (a.num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "%s: bad sizes", who);
+    if (!a.cu_seqlens && a.num_seqs != 1)
+        return fail(KDA_ERR_INVALID_ARG, "%s: cu_seqlens NULL needs num_seqs == 1", who);
+    if (!isfinite(a.scale)) return fail(KDA_ERR_INVALID_ARG, "%s: scale not finite", who);
+    if (a.o && (a.o == a.q || a.o == a.k || a.o == a.v || a.o == gate ||
+                a.o == (const void *)a.beta || a.o == (const void *)a.workspace ||
+                (gated && a.o && (a.o == (const void *)a.a_log || a.o == (const void *)a.dt_bias))))
+        return fail(KDA_ERR_INVALID_ARG, "%s: o aliases an input or the workspace", who);
+    if (!(a.gate_lb <= 0.f)) return fail(KDA_ERR_INVALID_ARG, "%s: gate bound > 0 or NaN", who);
+    if (a.gate_lb < -9.f) return fail(KDA_ERR_UNSUPPORTED, "%s: gate bound below -9", who);
+    kda_status_t st;
+    const int c = chunk_shape_check(who, a.total_tokens, a.heads, a.dk, a.dv, a.chunk, dtype,
+                                    out_dtype, &st);
+    if (c == 0) return st;
+    if ((int64_t)a.num_seqs * a.heads * (a.dv / 16) > ((int64_t)1 << 28) ||
+        (a.total_tokens + c - 1) / c > ((int64_t)1 << 31) - 1)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: grid too large", who);
+    if (a.total_tokens > 0 && workspace_bytes < kda::chunk_workspace_bytes(a.total_tokens, a.heads, c))
+        return fail(KDA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", who,
+                    workspace_bytes, kda::chunk_workspace_bytes(a.total_tokens, a.heads, c));
+    int used = 0;
+    return from_hip(chunk_launcher(dtype, out_dtype, gated)(a, (hipStream_t)stream, true, &used),
+                    who);
 }
 
 }  // namespace
@@ -150,35 +188,28 @@ KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, 
                                    void *workspace, size_t workspace_bytes, kda_dtype_t dtype,
                                    kda_dtype_t out_dtype, void *stream) {
     g_last_error[0] = '\0';
-    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o || !workspace))
-        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: NULL q/k/v/g/beta/o/workspace");
-    if (num_seqs < 1)
-        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: bad sizes");
-    if (!cu_seqlens && num_seqs != 1)
-        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: cu_seqlens NULL needs num_seqs == 1");
-    if (!isfinite(scale)) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: scale not finite");
-    if (o && (o == q || o == k || o == v || o == (const void *)g || o == (const void *)beta ||
-              o == workspace))
-        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: o aliases an input or the workspace");
-    if (!(gate_lower_bound <= 0.f)) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: gate bound > 0 or NaN");
-    if (gate_lower_bound < -9.f)
-        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: gate_lower_bound below -9");
-    kda_status_t st;
-    const int c = chunk_shape_check("kda_chunk_fwd", total_tokens, num_heads, dk, dv, chunk_size,
-                                    dtype, out_dtype, &st);
-    if (c == 0) return st;
-    if ((int64_t)num_seqs * num_heads * (dv / 16) > ((int64_t)1 << 28) ||
-        (total_tokens + c - 1) / c > ((int64_t)1 << 31) - 1)
-        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: grid too large");
-    if (total_tokens > 0 && workspace_bytes < kda::chunk_workspace_bytes(total_tokens, num_heads, c))
-        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: workspace of %zu bytes, %zu needed",
-                    workspace_bytes, kda::chunk_workspace_bytes(total_tokens, num_heads, c));
-    kda::ChunkArgs a{q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, dk, dv,
-                     chunk_size, scale, gate_lower_bound, initial_state, final_state, o,
-                     (float *)workspace};
-    int used = 0;
-    return from_hip(chunk_launcher(dtype, out_dtype)(a, (hipStream_t)stream, true, &used),
-                    "kda_chunk_fwd");
+    const kda::ChunkArgs a{q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, dk,
+                           dv, chunk_size, scale, gate_lower_bound, initial_state, final_state, o,
+                           (float *)workspace, nullptr, nullptr, nullptr};
+    return chunk_checked_launch("kda_chunk_fwd", a, g, false, workspace_bytes, dtype, out_dtype,
+                                stream);
+}
+
+KDA_API kda_status_t kda_chunk_fwd_gated(const void *q, const void *k, const void *v,
+                                         const void *z, const float *a_log, const float *dt_bias,
+                                         float lower_bound, const float *beta,
+                                         const int32_t *cu_seqlens, int32_t num_seqs,
+                                         int64_t total_tokens, int32_t num_heads, int32_t dk,
+                                         int32_t dv, int32_t chunk_size, float scale,
+                                         const float *initial_state, float *final_state, void *o,
+                                         void *workspace, size_t workspace_bytes,
+                                         kda_dtype_t dtype, kda_dtype_t out_dtype, void *stream) {
+    g_last_error[0] = '\0';
+    const kda::ChunkArgs a{q, k, v, nullptr, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+                           dk, dv, chunk_size, scale, lower_bound, initial_state, final_state, o,
+                           (float *)workspace, z, a_log, dt_bias};
+    return chunk_checked_launch("kda_chunk_fwd_gated", a, z, true, workspace_bytes, dtype,
+                                out_dtype, stream);
 }
 
 KDA_API kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const float *g,

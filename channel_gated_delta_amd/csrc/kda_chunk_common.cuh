@@ -51,6 +51,36 @@ __device__ __forceinline__ void st_off(void *base, uint32_t byte_off, V x) {
     *reinterpret_cast<V *>(reinterpret_cast<char *>(base) + byte_off) = x;
 }
 
+// Source of the log-decay g of every (token, head, key channel).  Plain: read
+// from g [T, H, dk] (fp32).  Fused bounded gate ([Walkthrough] 彩蛋: the gate
+// function with a lower bound): formed from the gate's pre-activation z
+// [T, H, dk] (activation dtype), a per-head A_log and a per-channel bias as
+//     g = lb * sigmoid(e^{A_log[h]} (z + dt_bias[h, c])),
+// so lb <= g <= 0 by construction.  The kernels take the source by value and a
+// compile-time switch GZ (true: the fused gate) telling which fields they read.
+struct GateSrc {
+    const float *g;        // plain gate
+    const void *z;         // fused gate: pre-activation
+    const float *a_log;    // [H], NULL = 0
+    const float *dt_bias;  // [H, dk], NULL = 0
+    float lb;              // fused gate: the lower bound
+};
+
+// The fused gate in log2 units, x = g log2(e).  With the (head, channel)
+// constants c1 = -log2(e) e^{A_log[h]} and c2 = c1 dt_bias[h, c], the sigmoid's
+// argument y satisfies -y log2(e) = z c1 + c2, so x = lb log2(e) / (1 + 2^{z c1 + c2}).
+// The hardware exp2 (+inf for large arguments: the sigmoid is then 0) and
+// reciprocal estimate are each within about one ulp.
+__device__ __forceinline__ float gate_c1(const GateSrc &gs, int h) {
+    return -kLog2e * (gs.a_log ? expf(gs.a_log[h]) : 1.f);
+}
+__device__ __forceinline__ float gate_c2(const GateSrc &gs, float c1, int h, int dk, int c) {
+    return gs.dt_bias ? c1 * gs.dt_bias[(size_t)h * dk + c] : 0.f;
+}
+__device__ __forceinline__ float gate_log2(float z, float c1, float c2, float lb_log2e) {
+    return lb_log2e * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(z, c1, c2)));
+}
+
 // Packed-sequence offset i clamped to [0, total]; cu == NULL is one sequence.
 __device__ __forceinline__ int64_t chunk_seq_off(const int32_t *cu, int i, int64_t total) {
     if (!cu) return i == 0 ? 0 : total;

@@ -40,26 +40,27 @@ int pick_chunk(int chunk) {
     return 0;
 }
 
-template <class T, class TO, int DK, int BV, int C>
+template <class T, class TO, int DK, int BV, int C, bool GZ>
 hipError_t run(const ChunkArgs &a, hipStream_t s) {
     if constexpr (!fits<T, DK, BV, C>()) {
         return hipErrorNotSupported;
     } else {
         float *tb = a.workspace;
+        const GateSrc gs{a.g, a.gz, a.a_log, a.dt_bias, a.gate_lb};
         float *pm = tb ? tb + (size_t)a.total_tokens * a.heads * C : nullptr;
         if (a.total_tokens > 0) {
             const int64_t ntiles = (a.total_tokens + C - 1) / C;
             if constexpr (std::is_same<T, bf16>::value && C == 16 && DK % 32 == 0) {
                 // one wave per (tile, head), four per workgroup
                 const int64_t units = ntiles * a.heads;
-                hipLaunchKernelGGL((chunk_prep16_kernel<DK>), dim3((unsigned)((units + 3) / 4)),
-                                   dim3(256), 0, s, (const bf16 *)a.q, (const bf16 *)a.k, a.g,
+                hipLaunchKernelGGL((chunk_prep16_kernel<DK, GZ>), dim3((unsigned)((units + 3) / 4)),
+                                   dim3(256), 0, s, (const bf16 *)a.q, (const bf16 *)a.k, gs,
                                    a.beta, a.cu_seqlens, a.num_seqs, a.total_tokens, a.heads,
                                    a.scale, units, tb, pm);
             } else {
                 const dim3 g1((unsigned)ntiles, (unsigned)a.heads);
-                hipLaunchKernelGGL((chunk_prep_kernel<T, DK, C>), g1, dim3(256), 0, s,
-                                   (const T *)a.q, (const T *)a.k, a.g, a.beta, a.cu_seqlens,
+                hipLaunchKernelGGL((chunk_prep_kernel<T, DK, C, GZ>), g1, dim3(256), 0, s,
+                                   (const T *)a.q, (const T *)a.k, gs, a.beta, a.cu_seqlens,
                                    a.num_seqs, a.total_tokens, a.heads, a.scale, tb, pm);
             }
             const hipError_t e = hipGetLastError();
@@ -69,25 +70,25 @@ hipError_t run(const ChunkArgs &a, hipStream_t s) {
         const int units = a.num_seqs * a.heads;
         const int nslice = a.dv / BV;
         const unsigned g2 = (unsigned)(((units + 7) / 8) * 8 * nslice);
-        hipLaunchKernelGGL((chunk_state_kernel<T, TO, DK, BV, C>), dim3(g2),
+        hipLaunchKernelGGL((chunk_state_kernel<T, TO, DK, BV, C, GZ>), dim3(g2),
                            dim3(StateCfg<T, DK, BV, C>::NT), 0, s,
-                           (const T *)a.q, (const T *)a.k, (const T *)a.v, a.g, tb, pm,
+                           (const T *)a.q, (const T *)a.k, (const T *)a.v, gs, tb, pm,
                            a.cu_seqlens, a.total_tokens, a.heads, a.dv, a.scale, a.h0, a.hT,
                            (TO *)a.o, units, nslice);
         return hipGetLastError();
     }
 }
 
-template <class T, class TO, int DK, int C>
+template <class T, class TO, int DK, int C, bool GZ>
 hipError_t run_bv(const ChunkArgs &a, hipStream_t s) {
     switch (pick_bv(a.dv)) {
-        case 64: return run<T, TO, DK, 64, C>(a, s);
-        case 32: return run<T, TO, DK, 32, C>(a, s);
-        default: return run<T, TO, DK, 16, C>(a, s);
+        case 64: return run<T, TO, DK, 64, C, GZ>(a, s);
+        case 32: return run<T, TO, DK, 32, C, GZ>(a, s);
+        default: return run<T, TO, DK, 16, C, GZ>(a, s);
     }
 }
 
-template <class T, class TO, int DK>
+template <class T, class TO, int DK, bool GZ>
 hipError_t run_dk(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used) {
     const int c = pick_chunk<T, DK>(a.chunk);
     *chunk_used = c;
@@ -95,22 +96,25 @@ hipError_t run_dk(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_use
     if (!launch) return hipSuccess;
     switch (c) {
 #if KDA_CHUNK_MAX >= 64
-        case 64: return run_bv<T, TO, DK, 64>(a, s);
+        case 64: return run_bv<T, TO, DK, 64, GZ>(a, s);
 #endif
-        case 32: return run_bv<T, TO, DK, 32>(a, s);
-        default: return run_bv<T, TO, DK, 16>(a, s);
+#if KDA_CHUNK_MAX >= 32
+        case 32: return run_bv<T, TO, DK, 32, GZ>(a, s);
+#endif
+        default: return run_bv<T, TO, DK, 16, GZ>(a, s);
     }
 }
 
-template <class T, class TO>
+// GZ: the fused bounded gate (ChunkArgs::gz and friends) instead of g.
+template <class T, class TO, bool GZ>
 hipError_t dispatch(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used) {
     *chunk_used = 0;
     if (a.dv != 16 && a.dv != 32 && a.dv != 64 && a.dv != 128) return hipErrorNotSupported;
     switch (a.dk) {
-        case 16: return run_dk<T, TO, 16>(a, s, launch, chunk_used);
-        case 32: return run_dk<T, TO, 32>(a, s, launch, chunk_used);
-        case 64: return run_dk<T, TO, 64>(a, s, launch, chunk_used);
-        case 128: return run_dk<T, TO, 128>(a, s, launch, chunk_used);
+        case 16: return run_dk<T, TO, 16, GZ>(a, s, launch, chunk_used);
+        case 32: return run_dk<T, TO, 32, GZ>(a, s, launch, chunk_used);
+        case 64: return run_dk<T, TO, 64, GZ>(a, s, launch, chunk_used);
+        case 128: return run_dk<T, TO, 128, GZ>(a, s, launch, chunk_used);
     }
     return hipErrorNotSupported;
 }

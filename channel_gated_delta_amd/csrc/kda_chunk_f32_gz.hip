@@ -1,0 +1,9 @@
+// Fp32 instantiations of the chunkwise prefill with the bounded
+// forget gate fused in (the kernels form g from the gate's pre-activation).
+#include "kda_chunk_dispatch.cuh"
+
+namespace kda {
+hipError_t launch_chunk_f32_gz(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used) {
+    return chunk_detail::dispatch<float, float, true>(a, s, launch, chunk_used);
+}
+}  // namespace kda

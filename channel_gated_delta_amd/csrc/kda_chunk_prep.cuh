@@ -64,10 +64,10 @@ struct PrepCfg {
     static constexpr int kMinWg = kLds <= 53 * 1024 ? 3 : (kLds <= 80 * 1024 ? 2 : 1);
 };
 
-template <class T, int DK, int C>
+template <class T, int DK, int C, bool GZ>
 __global__ __launch_bounds__(256, (PrepCfg<T, DK, C>::kMinWg))
-void chunk_prep_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                       const float *__restrict__ g, const float *__restrict__ beta,
+void chunk_prep_kernel(const T *__restrict__ q, const T *__restrict__ k, GateSrc gs,
+                       const float *__restrict__ beta,
                        const int32_t *__restrict__ cu_seqlens, int nseq, int64_t total, int H,
                        float scale, float *__restrict__ tb_out, float *__restrict__ p_out) {
     using Cfg = PrepCfg<T, DK, C>;
@@ -102,6 +102,14 @@ void chunk_prep_kernel(const T *__restrict__ q, const T *__restrict__ k,
     const size_t rowQK = (size_t)H * DK;
     const int cp = tid % NPC, part = tid / NPC;
     const bool fthread = part < NPART;
+    // fused gate: this thread's constants for channels 2cp, 2cp+1
+    float gc1 = 0.f, gc2a = 0.f, gc2b = 0.f, glb = 0.f;
+    if constexpr (GZ) {
+        gc1 = gate_c1(gs, h);
+        gc2a = gate_c2(gs, gc1, h, DK, 2 * cp);
+        gc2b = gate_c2(gs, gc1, h, DK, 2 * cp + 1);
+        glb = gs.lb * kLog2e;
+    }
 
     // The sequences overlapping [t0, t1): the first is the last n with cu[n] <= t0.
     int n = 0;
@@ -129,14 +137,22 @@ void chunk_prep_kernel(const T *__restrict__ q, const T *__restrict__ k,
         float qv[RP][2], kv[RP][2], gam[RP][2];
         if (fthread) {
             T2 qr[RP], kr[RP];
-            f32x2 gr[RP];
+            f32x2 gr[RP];   // log2-decay of the two channels
 #pragma unroll
             for (int j = 0; j < RP; ++j) {
                 const int r = min(part * RP + j, nt - 1);
                 const size_t off = (size_t)(cs + r) * rowQK + (size_t)h * DK + 2 * cp;
                 qr[j] = *reinterpret_cast<const T2 *>(q + off);
                 kr[j] = *reinterpret_cast<const T2 *>(k + off);
-                gr[j] = *reinterpret_cast<const f32x2 *>(g + off);
+                if constexpr (GZ) {
+                    const T2 zr = *reinterpret_cast<const T2 *>(static_cast<const T *>(gs.z) + off);
+                    gr[j][0] = gate_log2(to_f32(zr[0]), gc1, gc2a, glb);
+                    gr[j][1] = gate_log2(to_f32(zr[1]), gc1, gc2b, glb);
+                } else {
+                    const f32x2 gv = *reinterpret_cast<const f32x2 *>(gs.g + off);
+                    gr[j][0] = gv[0] * kLog2e;
+                    gr[j][1] = gv[1] * kLog2e;
+                }
             }
             float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -146,8 +162,8 @@ void chunk_prep_kernel(const T *__restrict__ q, const T *__restrict__ k,
                 qv[j][1] = in ? to_f32(qr[j][1]) : 0.f;
                 kv[j][0] = in ? to_f32(kr[j][0]) : 0.f;
                 kv[j][1] = in ? to_f32(kr[j][1]) : 0.f;
-                a0 += (in ? gr[j][0] : 0.f) * kLog2e;
-                a1 += (in ? gr[j][1] : 0.f) * kLog2e;
+                a0 += in ? gr[j][0] : 0.f;
+                a1 += in ? gr[j][1] : 0.f;
                 gam[j][0] = a0;
                 gam[j][1] = a1;
                 // exact diagonal of P: scale * q_r . k_r over the NPC lanes of this part
@@ -346,10 +362,10 @@ __device__ __forceinline__ float row_shr_zero(float v) {   // lane l%16 >= S: la
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + S, 0xf, 0xf, false));
 }
 
-template <int DK>
+template <int DK, bool GZ>
 __global__ __launch_bounds__(256, KDA_PREP16_MINB)
-void chunk_prep16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
-                         const float *__restrict__ g, const float *__restrict__ beta,
+void chunk_prep16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k, GateSrc gs,
+                         const float *__restrict__ beta,
                          const int32_t *__restrict__ cu_seqlens, int nseq, int64_t total, int H,
                          float scale, int64_t units, float *__restrict__ tb_out,
                          float *__restrict__ p_out) {
@@ -364,6 +380,11 @@ void chunk_prep16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int64_t t0 = (unit / H) * C, t1 = min(t0 + C, total);
     const size_t rowQK = (size_t)H * DK;
     const int t = lane & 15, kb = lane >> 4;
+    float gc1 = 0.f, glb = 0.f;   // fused gate: this head's constants
+    if constexpr (GZ) {
+        gc1 = gate_c1(gs, h);
+        glb = gs.lb * kLog2e;
+    }
 
     int n = 0;
     if (cu_seqlens) {
@@ -394,11 +415,25 @@ void chunk_prep16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         for (int j = 0; j < NKB; ++j) {
             const bf16x8 qr = *reinterpret_cast<const bf16x8 *>(q + off + 32 * j);
             const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(k + off + 32 * j);
-            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(g + off + 32 * j);
-            const f32x4 g1 = *reinterpret_cast<const f32x4 *>(g + off + 32 * j + 4);
             float x[8], qd[8], kd[8], kc[8];
+            if constexpr (GZ) {
+                const bf16x8 zr = *reinterpret_cast<const bf16x8 *>(
+                    static_cast<const bf16 *>(gs.z) + off + 32 * j);
+                const int c0 = 32 * j + 8 * kb;
+                f32x4 d0 = f32x4{0.f, 0.f, 0.f, 0.f}, d1 = d0;
+                if (gs.dt_bias) {
+                    d0 = *reinterpret_cast<const f32x4 *>(gs.dt_bias + (size_t)h * DK + c0);
+                    d1 = *reinterpret_cast<const f32x4 *>(gs.dt_bias + (size_t)h * DK + c0 + 4);
+                }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (e < 4 ? g0[e] : g1[e - 4]) * kLog2e;
+                for (int e = 0; e < 8; ++e)
+                    x[e] = gate_log2((float)zr[e], gc1, gc1 * (e < 4 ? d0[e] : d1[e - 4]), glb);
+            } else {
+                const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gs.g + off + 32 * j);
+                const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gs.g + off + 32 * j + 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = (e < 4 ? g0[e] : g1[e - 4]) * kLog2e;
+            }
             // inclusive prefix over the rows (G_t, log2 units)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {

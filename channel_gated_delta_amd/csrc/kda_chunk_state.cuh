@@ -244,10 +244,10 @@ __device__ __forceinline__ void state_chain_bf16(
     }
 }
 
-template <class T, class TO, int DK, int BV, int C>
+template <class T, class TO, int DK, int BV, int C, bool GZ>
 __global__ __launch_bounds__((StateCfg<T, DK, BV, C>::NT), 1)
 void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-                        const float *__restrict__ g, const float *__restrict__ tb,
+                        GateSrc gs, const float *__restrict__ tb,
                         const float *__restrict__ pm, const int32_t *__restrict__ cu_seqlens,
                         int64_t total, int H, int DV, float scale, const float *__restrict__ h0,
                         float *__restrict__ hT, TO *__restrict__ o, int units, int nslice) {
@@ -285,6 +285,13 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
         const int pt = tid - 4 * kWave;                       // 0 .. 255
         const int pw = wave - 4;
         const int cpair = pw * CPW + (lane % CPW);            // channels 2cpair, 2cpair+1
+        float gc1 = 0.f, gc2a = 0.f, gc2b = 0.f, glb = 0.f;   // fused gate constants
+        if constexpr (GZ) {
+            gc1 = gate_c1(gs, h);
+            gc2a = gate_c2(gs, gc1, h, DK, 2 * cpair);
+            gc2b = gate_c2(gs, gc1, h, DK, 2 * cpair + 1);
+            glb = gs.lb * kLog2e;
+        }
         const int rg = lane / CPW;                            // row group: rows rg*RP + j
         const bool act = rg < RG;
         const int tr = (pt * NTB) / C, tc = (pt * NTB) % C;   // Tb / P: row tr, cols tc..
@@ -297,7 +304,7 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
         constexpr int NTB4 = NTB >= 4 ? NTB / 4 : 1;
         struct Regs {
             T2 q[RP], k[RP];
-            f32x2 g[RP];
+            typename std::conditional<GZ, T2, f32x2>::type g[RP];   // g, or the gate's z
             f32x4 tb[NTB4], pm[NTB4];   // NTB == 1 uses element 0 of the first vector
             TV v;
         };
@@ -307,7 +314,8 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
             const int last = (int)min((int64_t)C, eos - cs) - 1;
             const size_t bq = (size_t)cs * rowQK + (size_t)h * DK;
             const T *qb = q + bq, *kb = k + bq;
-            const float *gb = g + bq;
+            const float *gb = gs.g + bq;
+            const T *zb = static_cast<const T *>(gs.z) + bq;
             if (act) {
 #pragma unroll
                 for (int j = 0; j < RP; ++j) {
@@ -315,7 +323,10 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                                          (uint32_t)(2 * cpair);
                     R.q[j] = ld_off<T2>(qb, off * (uint32_t)sizeof(T));
                     R.k[j] = ld_off<T2>(kb, off * (uint32_t)sizeof(T));
-                    R.g[j] = ld_off<f32x2>(gb, off * 4u);
+                    if constexpr (GZ)
+                        R.g[j] = ld_off<T2>(zb, off * (uint32_t)sizeof(T));
+                    else
+                        R.g[j] = ld_off<f32x2>(gb, off * 4u);
                 }
             }
             const float *tbb = tb + ((size_t)cs * H + h) * C, *pmb = pm + ((size_t)cs * H + h) * C;
@@ -355,8 +366,13 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                 qv[j][1] = to_f32(cur.q[j][1]);
                 kv[j][0] = to_f32(cur.k[j][0]);
                 kv[j][1] = to_f32(cur.k[j][1]);
-                a0 += (in ? cur.g[j][0] : 0.f) * kLog2e;
-                a1 += (in ? cur.g[j][1] : 0.f) * kLog2e;
+                if constexpr (GZ) {
+                    a0 += in ? gate_log2(to_f32(cur.g[j][0]), gc1, gc2a, glb) : 0.f;
+                    a1 += in ? gate_log2(to_f32(cur.g[j][1]), gc1, gc2b, glb) : 0.f;
+                } else {
+                    a0 += (in ? cur.g[j][0] : 0.f) * kLog2e;
+                    a1 += (in ? cur.g[j][1] : 0.f) * kLog2e;
+                }
                 gam[j][0] = a0;
                 gam[j][1] = a1;
             }

@@ -31,6 +31,10 @@ struct ChunkArgs {
     float *hT;
     void *o;        // output dtype chosen by the launcher called
     float *workspace;   // 2 * total_tokens * heads * C floats (C = the internal chunk)
+    // fused bounded gate (the *_gz launchers): pre-activation z [T, H, dk] in the
+    // activation dtype, A_log [H] and dt_bias [H, dk] (NULL = 0); gate_lb is its bound
+    const void *gz;
+    const float *a_log, *dt_bias;
 };
 
 // Workspace of the chunk prefill for internal chunk c: Tb and scale * P rows.
@@ -56,6 +60,10 @@ hipError_t launch_short_conv(const ConvArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_chunk_bf16_f32out(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
 hipError_t launch_chunk_bf16_bf16out(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
 hipError_t launch_chunk_f32(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
+// The same with the fused bounded gate (reads gz, a_log, dt_bias instead of g).
+hipError_t launch_chunk_bf16_f32out_gz(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
+hipError_t launch_chunk_bf16_bf16out_gz(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
+hipError_t launch_chunk_f32_gz(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
 typedef hipError_t (*ChunkLauncher)(const ChunkArgs &, hipStream_t, bool, int *);
 hipError_t launch_decode_step(const DecodeArgs &a, bool bf16, hipStream_t s);
 

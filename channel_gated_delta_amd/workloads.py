@@ -17,6 +17,9 @@ dtype; "N(0, s)" means standard deviation s):
 * initial state            N(0, 0.05)                    fp32   [N, H, D, D]
 * pre-processed q/k        N(0, 1) scaled to unit L2 length per (token, head)
   (the decode and tiny workloads feed the recurrence directly)
+* fused-gate inputs (make_gate, seed + 1000): pre-activation z N(0, gate_std) in
+  the activation dtype [T, H, D], A_log N(0, 0.3) fp32 [H], dt_bias N(0, 0.5)
+  fp32 [H, D]
 
 The pages' own workloads are a Kimi-K3 KDA layer: 96 heads of 128x128 state,
 width-4 short conv, gate floor -5; they publish no dataset or benchmark inputs.
@@ -141,6 +144,18 @@ def make_prefill(spec: PrefillSpec, device="cpu") -> Dict[str, torch.Tensor]:
     out["cu_seqlens"] = torch.tensor(cu_seqlens_of(spec.lengths), dtype=torch.int32,
                                      device=device)
     return out
+
+
+def make_gate(spec: PrefillSpec, device="cpu") -> Dict[str, torch.Tensor]:
+    """Inputs of the fused bounded gate for the same call: ``z`` [T, H, DK] in the
+    activation dtype, ``a_log`` [H] and ``dt_bias`` [H, DK] fp32 (own seed)."""
+    gen = _gen(device, spec.seed + 1000)
+    T, H, DK = spec.total_tokens, spec.heads, spec.dk
+    return {
+        "z": _normal((T, H, DK), gen, device, spec.gate_std).to(spec.dtype),
+        "a_log": _normal((H,), gen, device, 0.3).float(),
+        "dt_bias": _normal((H, DK), gen, device, 0.5).float(),
+    }
 
 
 def make_decode_state(spec: DecodeSpec, device="cpu") -> torch.Tensor:

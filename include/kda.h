@@ -157,6 +157,35 @@ KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, 
                            kda_dtype_t out_dtype, void *stream);
 
 /*
+ * kda_chunk_fwd_gated -- kda_chunk_fwd with the bounded forget gate fused in.
+ *
+ * Instead of the log-decay g the caller passes the gate's pre-activation z and
+ * its parameters; the kernels form, as they read each value,
+ *     g[t, h, c] = lower_bound * sigmoid(exp(a_log[h]) * (z[t, h, c] + dt_bias[h, c]))
+ * ([Walkthrough] 彩蛋: the gate function with a lower bound; K3 uses -5), in
+ * fp32 (hardware exp2 and reciprocal, a few ulps), so lower_bound <= g <= 0 by
+ * construction and g never goes through memory.  With bf16 activations z is
+ * bf16: half the bytes of g.
+ *
+ *   z        [total_tokens, num_heads, dk]  dtype
+ *   a_log    [num_heads] fp32, or NULL (0: no scaling)
+ *   dt_bias  [num_heads, dk] fp32, or NULL (0)
+ *   lower_bound  in [-9, 0]; it is also the chunk algorithm's gate floor.
+ * Every other argument, the workspace (kda_chunk_fwd_workspace_size), the
+ * supported shapes and the errors are those of kda_chunk_fwd; o must not alias
+ * z, a_log or dt_bias either.
+ */
+KDA_API kda_status_t kda_chunk_fwd_gated(const void *q, const void *k, const void *v,
+                                         const void *z, const float *a_log, const float *dt_bias,
+                                         float lower_bound, const float *beta,
+                                         const int32_t *cu_seqlens, int32_t num_seqs,
+                                         int64_t total_tokens, int32_t num_heads, int32_t dk,
+                                         int32_t dv, int32_t chunk_size, float scale,
+                                         const float *initial_state, float *final_state, void *o,
+                                         void *workspace, size_t workspace_bytes,
+                                         kda_dtype_t dtype, kda_dtype_t out_dtype, void *stream);
+
+/*
  * kda_chunk_fwd_workspace_size -- bytes of device workspace kda_chunk_fwd needs
  * for these sizes (written to *bytes): 2 * total_tokens * num_heads * C * 4,
  * where C is the internal chunk size chosen for (dtype, dk, dv, chunk_size).

@@ -28,8 +28,10 @@ def to64(t: torch.Tensor) -> np.ndarray:
     return t.detach().double().cpu().numpy()
 
 
-def gpu_prefill(inp, spec, chunk=None, out=None):
-    """HIP path: prologue (if the workload has raw projections) then chunk_fwd."""
+def gpu_prefill(inp, spec, chunk=None, out=None, gate=None):
+    """HIP path: prologue (if the workload has raw projections) then chunk_fwd, or
+    chunk_fwd_gated when ``gate`` (workloads.make_gate's z, a_log, dt_bias; the
+    last two may be None) is given."""
     H, DK, DV = spec.heads, spec.dk, spec.dv
     cu = inp["cu_seqlens"]
     if spec.conv:
@@ -40,14 +42,22 @@ def gpu_prefill(inp, spec, chunk=None, out=None):
         v, _ = kda.short_conv(inp["v_raw"], inp["w_v"], num_heads=H, head_dim=DV, cu_seqlens=cu)
     else:
         q, k, v = inp["q"], inp["k"], inp["v"]
-    o, hT = kda.chunk_fwd(q, k, v, inp["g"], inp["beta"], cu_seqlens=cu, scale=spec.read_scale,
-                          gate_lower_bound=spec.gate_lb, chunk_size=chunk or spec.chunk,
-                          initial_state=inp["h0"], out=out)
+    if gate is None:
+        o, hT = kda.chunk_fwd(q, k, v, inp["g"], inp["beta"], cu_seqlens=cu,
+                              scale=spec.read_scale, gate_lower_bound=spec.gate_lb,
+                              chunk_size=chunk or spec.chunk, initial_state=inp["h0"], out=out)
+    else:
+        o, hT = kda.chunk_fwd_gated(q, k, v, gate["z"], inp["beta"], a_log=gate.get("a_log"),
+                                    dt_bias=gate.get("dt_bias"), lower_bound=spec.gate_lb,
+                                    cu_seqlens=cu, scale=spec.read_scale,
+                                    chunk_size=chunk or spec.chunk, initial_state=inp["h0"],
+                                    out=out)
     return dict(q=q, k=k, v=v, o=o, hT=hT)
 
 
-def oracle_prefill(inp, spec, heads):
-    """Oracle on the sampled heads: fp64 prologue (conv + SiLU + L2) and recurrence."""
+def oracle_prefill(inp, spec, heads, gate=None):
+    """Oracle on the sampled heads: fp64 prologue (conv + SiLU + L2), the bounded
+    gate from ``gate``'s inputs if given (else the workload's g), the recurrence."""
     H, DK, DV = spec.heads, spec.dk, spec.dv
     cu = inp["cu_seqlens"].cpu().numpy()
     heads = list(heads)
@@ -72,7 +82,12 @@ def oracle_prefill(inp, spec, heads):
         q = to64(inp["q"][:, heads])
         k = to64(inp["k"][:, heads])
         v = to64(inp["v"][:, heads])
-    g = to64(inp["g"][:, heads])
+    if gate is None:
+        g = to64(inp["g"][:, heads])
+    else:
+        al, dt = gate.get("a_log"), gate.get("dt_bias")
+        g = oracle.bounded_gate(to64(gate["z"][:, heads]), None if al is None else to64(al[heads]),
+                                None if dt is None else to64(dt[heads]), spec.gate_lb)
     beta = to64(inp["beta"][:, heads])
     h0 = None if inp["h0"] is None else to64(inp["h0"][:, heads])
     o, hT = oracle.recurrent(q, k, v, g, beta, cu_seqlens=cu, scale=spec.read_scale, h0=h0)

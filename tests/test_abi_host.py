@@ -32,9 +32,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"kda_short_conv", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
-                          "kda_decode_step", "kda_status_string", "kda_last_error",
-                          "kda_version"}
+    assert set(names) == {"kda_short_conv", "kda_chunk_fwd", "kda_chunk_fwd_gated",
+                          "kda_chunk_fwd_workspace_size", "kda_decode_step",
+                          "kda_status_string", "kda_last_error", "kda_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -110,6 +110,37 @@ def test_workspace_size(lib):
 def test_chunk_fwd_rejects(lib, kw, status):
     assert chunk(lib, **kw) == status
     assert lib.kda_last_error()
+
+
+def chunk_gated(lib, **kw):
+    a = dict(q=P, k=P, v=P, z=ctypes.c_void_p(4096 * 3), al=NULL, dt=NULL, lb=-5.0, beta=P,
+             cu=NULL, N=1, T=64, H=2, dk=128, dv=128, chunk=64, scale=0.1, h0=NULL, hT=NULL,
+             o=ctypes.c_void_p(8192), ws=ctypes.c_void_p(1 << 20), wsb=1 << 30, dtype=BF16,
+             odt=F32)
+    a.update(kw)
+    return lib.kda_chunk_fwd_gated(a["q"], a["k"], a["v"], a["z"], a["al"], a["dt"], a["lb"],
+                                   a["beta"], a["cu"], a["N"], a["T"], a["H"], a["dk"], a["dv"],
+                                   a["chunk"], a["scale"], a["h0"], a["hT"], a["o"], a["ws"],
+                                   a["wsb"], a["dtype"], a["odt"], NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(z=NULL), kda.KDA_ERR_INVALID_ARG),
+    (dict(beta=NULL), kda.KDA_ERR_INVALID_ARG),
+    (dict(o=ctypes.c_void_p(4096 * 3)), kda.KDA_ERR_INVALID_ARG),   # o aliases z
+    (dict(al=ctypes.c_void_p(8192)), kda.KDA_ERR_INVALID_ARG),      # o aliases a_log
+    (dict(dt=ctypes.c_void_p(8192)), kda.KDA_ERR_INVALID_ARG),      # o aliases dt_bias
+    (dict(lb=0.5), kda.KDA_ERR_INVALID_ARG),
+    (dict(lb=float("nan")), kda.KDA_ERR_INVALID_ARG),
+    (dict(lb=-9.5), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dk=48), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=F32, odt=BF16), kda.KDA_ERR_UNSUPPORTED),
+    (dict(wsb=2 * 64 * 2 * 16 * 4 - 1), kda.KDA_ERR_INVALID_ARG),
+    (dict(N=2), kda.KDA_ERR_INVALID_ARG),
+])
+def test_chunk_fwd_gated_rejects(lib, kw, status):
+    assert chunk_gated(lib, **kw) == status
+    assert b"kda_chunk_fwd_gated" in lib.kda_last_error()
 
 
 def conv(lib, **kw):

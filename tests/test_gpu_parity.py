@@ -144,6 +144,58 @@ def test_final_state_in_place():
     assert torch.equal(st, ref["hT"]) and torch.equal(o, ref["o"])
 
 
+# ------------------------------------------------------------------ fused bounded gate
+
+def check_gated(spec, params=True, heads=None):
+    inp = workloads.make_prefill(spec, DEV)
+    gate = workloads.make_gate(spec, DEV)
+    if not params:
+        gate = dict(z=gate["z"], a_log=None, dt_bias=None)
+    got = gpu_prefill(inp, spec, gate=gate)
+    torch.cuda.synchronize()
+    heads = list(range(spec.heads)) if heads is None else list(heads)
+    ref = oracle_prefill(inp, spec, heads, gate=gate)
+    tol = tol_for(spec.dtype)
+    assert_parity("o (fused gate)", to64(got["o"][:, heads]), ref["o"], tol)
+    assert_parity("final state (fused gate)", to64(got["hT"][:, heads]), ref["hT"], tol)
+    return inp, gate, got
+
+
+@pytest.mark.parametrize("params", [True, False], ids=["alog_dt", "z_only"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_gated_ragged_varlen(params, dtype):
+    """g = lb sigmoid(e^{A_log} (z + dt_bias)) formed in the kernels, ragged packed batch, h0."""
+    note("fused gate %s params=%s" % (dtype, params))
+    check_gated(spec_of(RAGGED, H=2, dtype=dtype, h0=0.05, seed=31), params=params)
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 16)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_gated_head_dims(dk, dv, dtype):
+    note("fused gate dims dk=%d dv=%d %s" % (dk, dv, dtype))
+    check_gated(spec_of([200, 37], H=3, dk=dk, dv=dv, dtype=dtype, h0=0.1, seed=dk + 2 * dv))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_gated_strong_decay_and_prologue(dtype):
+    """Gate floor -8 with a wide pre-activation, behind the conv + SiLU + L2 prologue."""
+    check_gated(spec_of([300, 5, 129], H=2, dtype=dtype, conv=True, lb=-8.0, gate_std=2.0,
+                        h0=0.05, seed=33))
+
+
+def test_gated_matches_plain_gate():
+    """The fused path equals chunk_fwd fed with the same gate precomputed (fp32)."""
+    spec = spec_of([150, 66], H=2, h0=0.05, seed=34)
+    inp, gate, got = check_gated(spec)
+    g = oracle.bounded_gate(to64(gate["z"]), to64(gate["a_log"]), to64(gate["dt_bias"]),
+                            spec.gate_lb)
+    inp["g"] = torch.from_numpy(g).float().to(DEV)
+    plain = gpu_prefill(inp, spec)
+    torch.cuda.synchronize()
+    assert_parity("o fused vs plain", to64(got["o"]), to64(plain["o"]), 1e-3)
+    assert_parity("state fused vs plain", to64(got["hT"]), to64(plain["hT"]), 1e-3)
+
+
 # ------------------------------------------------------------------ prologue alone
 
 @pytest.mark.parametrize("width", [1, 2, 3, 4])

@@ -20,18 +20,20 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def run_prefill_workload(name, heads):
+def run_prefill_workload(name, heads, fused_gate=False):
     spec = workloads.standard_specs()[name]
-    note("workload %s: %d tokens, sampled heads %s" % (spec.name, spec.total_tokens, heads))
+    note("workload %s%s: %d tokens, sampled heads %s" %
+         (spec.name, " (fused gate)" if fused_gate else "", spec.total_tokens, heads))
     inp = workloads.make_prefill(spec, DEV)
-    got = gpu_prefill(inp, spec)
+    gate = workloads.make_gate(spec, DEV) if fused_gate else None
+    got = gpu_prefill(inp, spec, gate=gate)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(got["o"]).all()) and bool(torch.isfinite(got["hT"]).all())
     go = to64(got["o"][:, heads])
     gh = to64(got["hT"][:, heads])
     gp = {name: to64(got[name][:, heads]) for name in ("q", "k", "v")} if spec.conv else None
     del got
-    ref = oracle_prefill(inp, spec, heads)
+    ref = oracle_prefill(inp, spec, heads, gate=gate)
     tol = tol_for(spec.dtype)
     if gp is not None:
         assert_prologue(gp, ref, spec.dtype)
@@ -49,6 +51,12 @@ def test_tiny_fp32_workload_full():
 def test_prefill_workload():
     """B=1, T=4096, H=96, d=128, chunk 64, bf16, conv4+SiLU+L2 prologue, zero h0."""
     run_prefill_workload("prefill", [0, 41, 95])
+
+
+@pytest.mark.timeout(600)
+def test_prefill_workload_fused_gate():
+    """The prefill workload with the bounded gate formed in the kernels from bf16 z."""
+    run_prefill_workload("prefill", [5, 60], fused_gate=True)
 
 
 @pytest.mark.timeout(600)
