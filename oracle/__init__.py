@@ -28,6 +28,7 @@ Contents:
 * ``round_bf16``  (O1c) rounding of an interface tensor to bf16         -- C, fp64
 * ``prologue``    O1a + O1b (+ O1c) for one of q, k, v                 -- C, fp64
 * ``recurrent``   (O2) token-by-token KDA recurrence                   -- C, fp64
+* ``output_norm_gate`` (O3) per-head RMSNorm times the sigmoid output gate -- C, fp64
 * ``oracle.chunked.chunked_forward``: an independently derived chunkwise
   form, used only as a brute-force pin of ``recurrent`` on tiny inputs.
 
@@ -102,6 +103,9 @@ class OracleLib:
         lib.kda_oracle_bounded_gate.argtypes = [
             _dp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _dp, _dp, ctypes.c_double, _dp]
         lib.kda_oracle_bounded_gate.restype = None
+        lib.kda_oracle_output_norm_gate.argtypes = [
+            _dp, _dp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _dp, ctypes.c_double, _dp]
+        lib.kda_oracle_output_norm_gate.restype = None
         lib.kda_oracle_num_threads.argtypes = []
         lib.kda_oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -182,6 +186,19 @@ class OracleLib:
         y = y.reshape(T, H, D)
         return (y, st) if return_state else y
 
+    def output_norm_gate(self, o, gate, w=None, eps: float = 1e-6):
+        """O3: y = o / sqrt(mean(o^2) + eps) * w * sigmoid(gate), per (token, head) row.
+
+        o, gate: [T, H, D]; w: [D] or None (1).  Returns y [T, H, D].
+        """
+        o, gate = _f64(o), _f64(gate)
+        T, H, D = o.shape
+        wa = None if w is None else _f64(w).reshape(D)
+        y = np.empty((T, H, D))
+        self.lib.kda_oracle_output_norm_gate(_ptr(o), _ptr(gate), T, H, D, _ptr(wa), float(eps),
+                                             _ptr(y))
+        return y
+
     def recurrent(self, q, k, v, g, beta, cu_seqlens=None, scale: float = 1.0, h0=None,
                   delta_rule: bool = True):
         """O2: the KDA recurrence, token by token, in fp64.
@@ -244,6 +261,10 @@ def round_bf16(*a, **kw):
 
 def recurrent(*a, **kw):
     return default().recurrent(*a, **kw)
+
+
+def output_norm_gate(*a, **kw):
+    return default().output_norm_gate(*a, **kw)
 
 
 def rel_err(got, ref) -> float:

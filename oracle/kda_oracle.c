@@ -114,6 +114,27 @@ void kda_oracle_bounded_gate(const double *z, int64_t T, int H, int D, const dou
 }
 
 /*
+ * O3. Output epilogue ([Walkthrough] 第六站: the read-out passes a per-head
+ *     RMSNorm, then the output gate scales it channel by channel, before the
+ *     output projection).  Per (token t, head h) row of D channels:
+ *         y[c] = o[c] / sqrt(mean_c' o[c']^2 + eps) * w[c] * sigmoid(gate[c]),
+ *     the gate being the output gate's pre-activation (its projection of the
+ *     layer input is outside the path) and w the norm's per-channel weight.
+ * o, gate, y: [T, H, D]; w: [D] or NULL (1).
+ */
+void kda_oracle_output_norm_gate(const double *o, const double *gate, int64_t T, int H, int D,
+                                 const double *w, double eps, double *y) {
+    for (int64_t r = 0; r < T * H; ++r) {
+        const double *orow = o + r * D, *grow = gate + r * D;
+        double ss = 0.0;
+        for (int c = 0; c < D; ++c) ss += orow[c] * orow[c];
+        const double inv = 1.0 / sqrt(ss / D + eps);
+        for (int c = 0; c < D; ++c)
+            y[r * D + c] = orow[c] * inv * (w ? w[c] : 1.0) / (1.0 + exp(-grow[c]));
+    }
+}
+
+/*
  * O1b. L2 normalisation of q and k ([Walkthrough] 第二站: after conv+SiLU the
  *      query and key are scaled to (close to) unit length; the operator does it).
  * x: [rows, D], each row scaled in place by 1 / sqrt(sum_c x_c^2 + eps).

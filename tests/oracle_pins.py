@@ -383,9 +383,41 @@ def pin_bounded_gate(orc):
     assert np.all(np.diff(g[:, 0, 0]) <= 0.0), "gate not decreasing in z"
 
 
+def pin_output_norm_gate(orc):
+    """Walkthrough 第六站: per-head RMSNorm of the read-out, then the sigmoid output gate.
+
+    A constant row c normalises to sign(c) (eps = 0); gate 0 halves and gate ln 3
+    keeps three quarters; the norm is per (token, head) and invariant to the row's
+    scale; the normalised row has unit root-mean-square.
+    """
+    ln3 = np.log(3.0)
+    T, H, D = 2, 3, 8
+    o = np.empty((T, H, D))
+    for t in range(T):
+        for h in range(H):
+            o[t, h] = (-1.0) ** (t + h) * 10.0 ** (h - 1)       # constant rows, scales 0.1 .. 10
+    gate = np.zeros((T, H, D))
+    gate[1] = ln3
+    w = 1.0 + 0.25 * np.arange(D)
+    y = orc.output_norm_gate(o, gate, w, eps=0.0)
+    for t, f in enumerate((0.5, 0.75)):
+        for h in range(H):
+            _close(y[t, h], np.sign(o[t, h]) * w * f, 1e-14, "constant row t=%d h=%d" % (t, h))
+    rng = np.random.default_rng(23)
+    o = rng.standard_normal((4, H, D)) * np.array([0.01, 1.0, 50.0])[None, :, None]
+    gate = rng.standard_normal((4, H, D))
+    y = orc.output_norm_gate(o, gate, None, eps=0.0)
+    _close(orc.output_norm_gate(7.5 * o, gate, None, eps=0.0), y, 1e-13, "scale invariance")
+    yn = y * (1.0 + np.exp(-gate))                      # undo the gate: unit-rms rows
+    _close(np.sqrt(np.mean(yn * yn, axis=-1)), np.ones((4, H)), 1e-13, "unit rms per row")
+    ref = o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + 1e-3) / (1.0 + np.exp(-gate))
+    _close(orc.output_norm_gate(o, gate, None, eps=1e-3), ref, 1e-13, "eps inside the root")
+
+
 ALL_PINS = [
     pin_unit_key_example, pin_one_dim_example, pin_two_address_example, pin_update_order,
     pin_identity, pin_pure_decay, pin_overwrite, pin_linear_attention, pin_gated_form,
     pin_chunked_matches_recurrent, pin_causality, pin_conv_library, pin_l2norm, pin_round_bf16,
     pin_varlen_and_resume, pin_value_columns_independent, pin_k3_sizes, pin_bounded_gate,
+    pin_output_norm_gate,
 ]

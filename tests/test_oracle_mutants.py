@@ -60,6 +60,15 @@ MUTANTS = {
     "gate_bias_per_head": [("dt_bias[(int64_t)h * D + c]", "dt_bias[h]")],
     "gate_sigmoid_sign": [("g[i] = lower_bound / (1.0 + exp(-y));", "g[i] = lower_bound / (1.0 + exp(y));")],
     "gate_bound_dropped": [("g[i] = lower_bound / (1.0 + exp(-y));", "g[i] = -1.0 / (1.0 + exp(-y));")],
+    "norm_no_mean": [("const double inv = 1.0 / sqrt(ss / D + eps);", "const double inv = 1.0 / sqrt(ss + eps);")],
+    "norm_no_sqrt": [("const double inv = 1.0 / sqrt(ss / D + eps);", "const double inv = 1.0 / (ss / D + eps);")],
+    "norm_eps_outside": [("const double inv = 1.0 / sqrt(ss / D + eps);", "const double inv = 1.0 / (sqrt(ss / D) + eps);")],
+    "norm_over_all_heads": [("for (int c = 0; c < D; ++c) ss += orow[c] * orow[c];",
+                             "for (int c = 0; c < D; ++c) ss += o[(r / H) * H * D + c] * o[(r / H) * H * D + c];")],
+    "out_gate_not_sigmoid": [("y[r * D + c] = orow[c] * inv * (w ? w[c] : 1.0) / (1.0 + exp(-grow[c]));",
+                              "y[r * D + c] = orow[c] * inv * (w ? w[c] : 1.0) * grow[c];")],
+    "out_weight_dropped": [("y[r * D + c] = orow[c] * inv * (w ? w[c] : 1.0) / (1.0 + exp(-grow[c]));",
+                            "y[r * D + c] = orow[c] * inv / (1.0 + exp(-grow[c]));")],
 }
 
 
