@@ -17,6 +17,8 @@ written).  ``value`` is prefill tokens/s.  The same JSON line carries:
 * ``fused_gate``: the same prefill step with the bounded gate formed inside the
   chunk kernels from bf16 pre-activations (kda_chunk_fwd_gated) instead of a
   precomputed fp32 g, and that call's roofline;
+* ``output_epilogue``: the per-head RMSNorm and sigmoid output gate applied to the
+  step's fp32 read-out (bf16 gate in, bf16 y out), timed alone, and its roofline;
 * ``cpu_baseline``: the fp64 oracle (prologue + recurrence) timed on this host's
   cores over the same workload, repeated for at least ten seconds.
 
@@ -45,6 +47,7 @@ KERNEL_SOURCES = {
     "decode": ("kda_device.cuh", "kda_decode.hip"),
     "gated": ("kda_device.cuh", "kda_chunk_common.cuh", "kda_chunk_prep.cuh",
               "kda_chunk_state.cuh", "kda_chunk_dispatch.cuh", "kda_chunk_bf16_gz.hip"),
+    "epilogue": ("kda_device.cuh", "kda_epilogue.hip"),
 }
 
 
@@ -87,6 +90,28 @@ def gated_step_bytes(T: int, H: int, dk: int, dv: int, N: int, h0: bool) -> floa
     """As prefill_step_bytes with the gate's bf16 pre-activation z (2*dk per token and
     head) in place of the fp32 g; A_log and dt_bias are negligible."""
     return prefill_step_bytes(T, H, dk, dv, N, h0) - float(T * H * 2 * dk)
+
+
+def epilogue_bytes(T: int, H: int, dv: int) -> float:
+    """Output epilogue: read o (fp32) and the gate (bf16), write y (bf16)."""
+    return float(T * H * dv * (4 + 2 + 2))
+
+
+def run_epilogue(args, torch, kda, workloads, o):
+    spec = workloads.standard_specs()[args.workload]
+    ep = workloads.make_epilogue(spec, "cuda:0")
+    y = torch.empty_like(ep["gate"])
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        kda.output_norm_gate(o, ep["gate"], ep["weight"], out=y)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        kda.output_norm_gate(o, ep["gate"], ep["weight"], out=y)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / args.steps
 
 
 def prologue_bytes(T: int, H: int, d: int) -> float:
@@ -154,7 +179,7 @@ def run_prefill(args, torch, kda, workloads, gated=False):
     total_ms = t_start.elapsed_time(t_end)
     chunk_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
     ms_step = total_ms / args.steps
-    return dict(spec=spec, T=T, N=N, ms_step=ms_step, chunk_ms=chunk_ms, inp=inp)
+    return dict(spec=spec, T=T, N=N, ms_step=ms_step, chunk_ms=chunk_ms, inp=inp, o=ob)
 
 
 def run_decode(torch, kda, workloads, steps=256, warmup=16):
@@ -244,6 +269,7 @@ def main():
     ap.add_argument("--workload", default="prefill", choices=["prefill", "varlen", "long"])
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-gate", action="store_true")
+    ap.add_argument("--no-epilogue", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (torch elementwise kernel), the "
@@ -318,6 +344,18 @@ def main():
                          "kernel": "kda_chunk_fwd_gated", "algorithmic_bytes_per_launch": gbytes,
                          "avg_launch_ms": round(gres["chunk_ms"], 4)}}
         del gres
+    if not args.no_epilogue:
+        ems = run_epilogue(args, torch, kda, workloads, res["o"])
+        ebytes = epilogue_bytes(T, H, DV)
+        each = ebytes / (ems / 1e3) / 1e9
+        out["output_epilogue"] = {
+            "ms_per_call": round(ems, 4),
+            "path": "kda_output_norm_gate: y = o / sqrt(mean(o^2) + eps) * w * sigmoid(gate), "
+                    "fp32 o, bf16 gate and y",
+            "roofline": {"bound": "hbm", "achieved": round(each, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(each / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("epilogue", args.workload),
+                         "kernel": "norm_gate_kernel", "algorithmic_bytes_per_launch": ebytes}}
     out["prologue_ms_per_step"] = round(res["ms_step"] - res["chunk_ms"], 4)
     out["prologue_bytes_per_step"] = prologue_bytes(T, H, DK)
     if not args.no_cpu:

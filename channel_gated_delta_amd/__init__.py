@@ -8,6 +8,7 @@ fallback: if libkda.so is missing the calls raise.
     short_conv(x, weight, ...)              -> (y, conv_state)   conv4 + SiLU (+ L2)
     chunk_fwd(q, k, v, g, beta, ...)        -> (o, final_state)  chunkwise prefill
     chunk_fwd_gated(q, k, v, z, beta, ...)  -> (o, final_state)  the same, bounded gate fused
+    output_norm_gate(o, gate, weight, ...)  -> y                 per-head RMSNorm * sigmoid gate
     decode_step(q, k, v, g, beta, state)    -> o                 one recurrent step
 
 Build the library with ``python -m channel_gated_delta_amd.build``.
@@ -21,7 +22,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["KdaError", "library", "short_conv", "chunk_fwd", "chunk_fwd_gated", "decode_step",
-           "LIB_PATH"]
+           "output_norm_gate", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -55,12 +56,14 @@ def library() -> ctypes.CDLL:
         lib.kda_chunk_fwd_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32,
                                             _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
                                             _vp, ctypes.c_size_t, _i32, _i32, _vp]
+        lib.kda_output_norm_gate.argtypes = [_vp, _vp, _vp, _f32, _i64, _i32, _i32, _i32, _vp,
+                                             _vp]
         lib.kda_chunk_fwd_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _i32,
                                                      ctypes.POINTER(ctypes.c_size_t)]
         lib.kda_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
                                         _vp, _i32, _i32, _vp]
         for fn in ("kda_short_conv", "kda_chunk_fwd", "kda_chunk_fwd_gated",
-                   "kda_chunk_fwd_workspace_size", "kda_decode_step"):
+                   "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_output_norm_gate"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_status_string.restype = ctypes.c_char_p
@@ -235,6 +238,29 @@ def _chunk(q, k, v, g, gate, beta, cu_seqlens, scale, lower_bound, chunk_size, i
             _ptr(initial_state), _ptr(final_state), _ptr(o), _ptr(workspace), workspace.numel(),
             _DTYPES[dt], _DTYPES[out_dtype], _stream(q)))
     return o, final_state
+
+
+def output_norm_gate(o: torch.Tensor, gate: torch.Tensor, weight: Optional[torch.Tensor] = None,
+                     *, eps: float = 1e-6, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = o / sqrt(mean(o^2) + eps) * weight * sigmoid(gate) per (token, head) row.
+
+    o: [..., dv] (fp32 or bf16); gate: same shape in the activation dtype (bf16 or
+    fp32), which y takes; weight: [dv] fp32 or None.  ``out`` may be ``gate``.
+    """
+    _dev(o, "o")
+    _dev(gate, "gate", None, tuple(o.shape))
+    if o.dtype not in _DTYPES or gate.dtype not in _DTYPES:
+        raise ValueError("o and gate must be bf16 or fp32")
+    dv = o.shape[-1]
+    if weight is not None:
+        _dev(weight, "weight", torch.float32, (dv,))
+    y = out if out is not None else torch.empty_like(gate)
+    _dev(y, "out", gate.dtype, tuple(o.shape))
+    rows = o.numel() // dv if dv else 0
+    _check(library().kda_output_norm_gate(_ptr(o), _ptr(gate), _ptr(weight), float(eps), rows,
+                                          dv, _DTYPES[o.dtype], _DTYPES[gate.dtype], _ptr(y),
+                                          _stream(o)))
+    return y
 
 
 def chunk_workspace_bytes(total_tokens: int, num_heads: int, dk: int, dv: int,

@@ -212,6 +212,33 @@ KDA_API kda_status_t kda_chunk_fwd_gated(const void *q, const void *k, const voi
                                 out_dtype, stream);
 }
 
+KDA_API kda_status_t kda_output_norm_gate(const void *o, const void *gate, const float *weight,
+                                          float eps, int64_t rows, int32_t dv,
+                                          kda_dtype_t o_dtype, kda_dtype_t dtype, void *y,
+                                          void *stream) {
+    g_last_error[0] = '\0';
+    if (rows > 0 && (!o || !gate || !y))
+        return fail(KDA_ERR_INVALID_ARG, "kda_output_norm_gate: NULL o/gate/y");
+    if (rows < 0) return fail(KDA_ERR_INVALID_ARG, "kda_output_norm_gate: bad sizes");
+    if (!valid_dtype(o_dtype) || !valid_dtype(dtype))
+        return fail(KDA_ERR_INVALID_ARG, "kda_output_norm_gate: bad dtype");
+    if (!(eps >= 0.f && isfinite(eps)))
+        return fail(KDA_ERR_INVALID_ARG, "kda_output_norm_gate: eps negative or not finite");
+    if (o && o == y && o_dtype != dtype)
+        return fail(KDA_ERR_INVALID_ARG, "kda_output_norm_gate: y aliases o of another dtype");
+    if (y && (y == (const void *)weight))
+        return fail(KDA_ERR_INVALID_ARG, "kda_output_norm_gate: y aliases the weight");
+    if (!head_dim_ok(dv)) return fail(KDA_ERR_UNSUPPORTED, "kda_output_norm_gate: dv not in {16,32,64,128}");
+    if (o_dtype == KDA_DTYPE_BF16 && dtype != KDA_DTYPE_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "kda_output_norm_gate: bf16 o needs a bf16 gate and y");
+    if ((rows * (dv / 4) + 255) / 256 > ((int64_t)1 << 31) - 1)
+        return fail(KDA_ERR_UNSUPPORTED, "kda_output_norm_gate: grid too large");
+    const kda::NormGateArgs a{o, gate, weight, eps, rows, dv, y};
+    return from_hip(kda::launch_norm_gate(a, o_dtype == KDA_DTYPE_BF16, dtype == KDA_DTYPE_BF16,
+                                          (hipStream_t)stream),
+                    "kda_output_norm_gate");
+}
+
 KDA_API kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const float *g,
                                      const float *beta, float *state, int32_t batch,
                                      int32_t num_heads, int32_t dk, int32_t dv, float scale,

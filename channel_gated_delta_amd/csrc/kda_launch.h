@@ -42,6 +42,15 @@ inline size_t chunk_workspace_bytes(int64_t total_tokens, int32_t heads, int c) 
     return (size_t)2 * (size_t)total_tokens * (size_t)heads * (size_t)c * sizeof(float);
 }
 
+struct NormGateArgs {
+    const void *o, *gate;
+    const float *weight;   // [dv] or NULL
+    float eps;
+    int64_t rows;          // tokens * heads
+    int32_t dv;
+    void *y;
+};
+
 struct DecodeArgs {
     const void *q, *k, *v;
     const float *g, *beta;
@@ -66,5 +75,7 @@ hipError_t launch_chunk_bf16_bf16out_gz(const ChunkArgs &a, hipStream_t s, bool 
 hipError_t launch_chunk_f32_gz(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
 typedef hipError_t (*ChunkLauncher)(const ChunkArgs &, hipStream_t, bool, int *);
 hipError_t launch_decode_step(const DecodeArgs &a, bool bf16, hipStream_t s);
+// o_bf16: o is bf16 (needs bf16 gate / y); y_bf16: gate and y are bf16.
+hipError_t launch_norm_gate(const NormGateArgs &a, bool o_bf16, bool y_bf16, hipStream_t s);
 
 }  // namespace kda

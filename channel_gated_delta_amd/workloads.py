@@ -20,6 +20,8 @@ dtype; "N(0, s)" means standard deviation s):
 * fused-gate inputs (make_gate, seed + 1000): pre-activation z N(0, gate_std) in
   the activation dtype [T, H, D], A_log N(0, 0.3) fp32 [H], dt_bias N(0, 0.5)
   fp32 [H, D]
+* output-epilogue inputs (make_epilogue, seed + 2000): output-gate pre-activation
+  N(0, 1) in the activation dtype [T, H, DV], norm weight 1 + N(0, 0.1) fp32 [DV]
 
 The pages' own workloads are a Kimi-K3 KDA layer: 96 heads of 128x128 state,
 width-4 short conv, gate floor -5; they publish no dataset or benchmark inputs.
@@ -144,6 +146,18 @@ def make_prefill(spec: PrefillSpec, device="cpu") -> Dict[str, torch.Tensor]:
     out["cu_seqlens"] = torch.tensor(cu_seqlens_of(spec.lengths), dtype=torch.int32,
                                      device=device)
     return out
+
+
+def make_epilogue(spec: PrefillSpec, device="cpu") -> Dict[str, torch.Tensor]:
+    """Inputs of the output epilogue for the same call: the output gate's
+    pre-activation ``gate`` [T, H, DV] (activation dtype) and the norm ``weight``
+    [DV] fp32 (own seed)."""
+    gen = _gen(device, spec.seed + 2000)
+    T, H, DV = spec.total_tokens, spec.heads, spec.dv
+    return {
+        "gate": _normal((T, H, DV), gen, device).to(spec.dtype),
+        "weight": (1.0 + _normal((DV,), gen, device, 0.1)).float(),
+    }
 
 
 def make_gate(spec: PrefillSpec, device="cpu") -> Dict[str, torch.Tensor]:

@@ -218,6 +218,28 @@ KDA_API kda_status_t kda_decode_step(const void *q, const void *k, const void *v
                              int32_t dk, int32_t dv, float scale, void *o, kda_dtype_t dtype,
                              kda_dtype_t out_dtype, void *stream);
 
+/*
+ * kda_output_norm_gate -- the read-out's exit path before the output projection
+ * ([Walkthrough] 第六站: a per-head RMSNorm, then the output gate scales each
+ * channel).  For every row r (a (token, head) pair) of dv channels:
+ *     y[r, c] = o[r, c] / sqrt(mean_c' o[r, c']^2 + eps) * weight[c] * sigmoid(gate[r, c])
+ * in fp32, rounded once to the dtype of y.  The sigmoid is the reading taken
+ * for the gate's nonlinearity (the pages name none); the gate's projection of
+ * the layer input and the output projection are outside this library.
+ *
+ *   o       [rows, dv]  o_dtype (the read-out of kda_chunk_fwd or kda_decode_step)
+ *   gate    [rows, dv]  dtype: the output gate's pre-activation
+ *   weight  [dv] fp32 (the norm's per-channel weight, shared by the heads), or NULL (1)
+ *   y       [rows, dv]  dtype; may be the same buffer as gate, or as o when o_dtype
+ *           equals dtype; no other overlap with an input is allowed.
+ * rows = tokens * heads (for o of shape [T, H, dv]).  Supported: dv in
+ * {16, 32, 64, 128}; eps >= 0; a bf16 o needs dtype bf16.
+ */
+KDA_API kda_status_t kda_output_norm_gate(const void *o, const void *gate, const float *weight,
+                                          float eps, int64_t rows, int32_t dv,
+                                          kda_dtype_t o_dtype, kda_dtype_t dtype, void *y,
+                                          void *stream);
+
 /* Static description of a status code (never NULL). */
 KDA_API const char *kda_status_string(kda_status_t status);
 

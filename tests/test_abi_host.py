@@ -34,7 +34,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"kda_short_conv", "kda_chunk_fwd", "kda_chunk_fwd_gated",
                           "kda_chunk_fwd_workspace_size", "kda_decode_step",
-                          "kda_status_string", "kda_last_error", "kda_version"}
+                          "kda_output_norm_gate", "kda_status_string", "kda_last_error",
+                          "kda_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -182,6 +183,29 @@ def test_decode_step_rejects(lib, kw, status):
     a.update(kw)
     assert lib.kda_decode_step(P, P, P, P, P, a["state"], a["B"], a["H"], a["dk"], a["dv"], 0.1,
                                a["o"], a["dtype"], a["odt"], NULL) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=NULL), kda.KDA_ERR_INVALID_ARG),
+    (dict(gate=NULL), kda.KDA_ERR_INVALID_ARG),
+    (dict(y=NULL), kda.KDA_ERR_INVALID_ARG),
+    (dict(rows=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(eps=-1.0), kda.KDA_ERR_INVALID_ARG),
+    (dict(eps=float("inf")), kda.KDA_ERR_INVALID_ARG),
+    (dict(odt=7), kda.KDA_ERR_INVALID_ARG),
+    (dict(y=P), kda.KDA_ERR_INVALID_ARG),                      # fp32 o, bf16 y in the same place
+    (dict(w=ctypes.c_void_p(8192)), kda.KDA_ERR_INVALID_ARG),  # y aliases the weight
+    (dict(dv=48), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dv=256), kda.KDA_ERR_UNSUPPORTED),
+    (dict(odt=BF16, dt=F32), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_output_norm_gate_rejects(lib, kw, status):
+    a = dict(o=P, gate=ctypes.c_void_p(4096 * 3), w=NULL, eps=1e-6, rows=64, dv=128, odt=F32,
+             dt=BF16, y=ctypes.c_void_p(8192))
+    a.update(kw)
+    assert lib.kda_output_norm_gate(a["o"], a["gate"], a["w"], a["eps"], a["rows"], a["dv"],
+                                    a["odt"], a["dt"], a["y"], NULL) == status
+    assert b"kda_output_norm_gate" in lib.kda_last_error()
 
 
 def test_binding_refuses_cpu_tensors():

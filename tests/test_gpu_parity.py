@@ -196,6 +196,53 @@ def test_gated_matches_plain_gate():
     assert_parity("state fused vs plain", to64(got["hT"]), to64(plain["hT"]), 1e-3)
 
 
+# ------------------------------------------------------------------ output epilogue
+
+def check_norm_gate(o, gate, w, eps):
+    y = kda.output_norm_gate(o, gate, w, eps=eps)
+    torch.cuda.synchronize()
+    ref = oracle.output_norm_gate(to64(o), to64(gate), None if w is None else to64(w), eps)
+    got = to64(y)
+    if y.dtype == torch.bfloat16:
+        # one rounding to bf16 (2^-9 relative) on top of fp32 arithmetic
+        bound = 2.0 ** -8 * np.abs(ref) + 1e-6 * float(np.sqrt(np.mean(ref * ref)))
+    else:
+        bound = 1e-5 * np.abs(ref) + 1e-6 * float(np.sqrt(np.mean(ref * ref)))
+    excess = np.abs(got - ref) - bound
+    assert np.all(excess <= 0), "max excess %.3e" % float(np.max(excess))
+    return y
+
+
+@pytest.mark.parametrize("dv", [16, 32, 64, 128])
+@pytest.mark.parametrize("odt,dt", [(torch.float32, torch.bfloat16), (torch.bfloat16, torch.bfloat16),
+                                    (torch.float32, torch.float32)], ids=["f32o_bf16", "bf16", "fp32"])
+def test_output_norm_gate(dv, odt, dt):
+    """Per-head RMSNorm * sigmoid gate, element by element against the oracle; ragged
+    row count, rows of very different scale, with and without the weight."""
+    note("output_norm_gate dv=%d o=%s y=%s" % (dv, odt, dt))
+    g = torch.Generator(device=DEV).manual_seed(50 + dv)
+    T, H = 37, 3
+    scale = torch.tensor([1e-3, 1.0, 30.0], device=DEV).view(1, H, 1)
+    o = (torch.randn(T, H, dv, generator=g, device=DEV) * scale).to(odt)
+    gate = (2.0 * torch.randn(T, H, dv, generator=g, device=DEV)).to(dt)
+    w = 1.0 + 0.5 * torch.randn(dv, generator=g, device=DEV)
+    check_norm_gate(o, gate, w, 1e-6)
+    check_norm_gate(o, gate, None, 0.0)
+
+
+def test_output_norm_gate_in_place_and_empty():
+    g = torch.Generator(device=DEV).manual_seed(60)
+    o = torch.randn(130, 96, 128, generator=g, device=DEV)
+    gate = torch.randn(130, 96, 128, generator=g, device=DEV).bfloat16()
+    w = torch.rand(128, generator=g, device=DEV) + 0.5
+    ref = kda.output_norm_gate(o, gate, w)
+    kda.output_norm_gate(o, gate, w, out=gate)          # y takes the gate's place
+    torch.cuda.synchronize()
+    assert torch.equal(gate, ref)
+    e = torch.empty(0, 4, 64, device=DEV)
+    assert kda.output_norm_gate(e, e.bfloat16()).numel() == 0
+
+
 # ------------------------------------------------------------------ prologue alone
 
 @pytest.mark.parametrize("width", [1, 2, 3, 4])

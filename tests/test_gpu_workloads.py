@@ -60,6 +60,28 @@ def test_prefill_workload_fused_gate():
 
 
 @pytest.mark.timeout(600)
+def test_prefill_workload_output_epilogue():
+    """The prefill read-out (fp32 o) through the per-head RMSNorm and sigmoid output gate
+    (bf16 y), in the configuration bench.py times; sampled heads element by element."""
+    spec = workloads.standard_specs()["prefill"]
+    inp = workloads.make_prefill(spec, DEV)
+    ep = workloads.make_epilogue(spec, DEV)
+    got = gpu_prefill(inp, spec)
+    y = kda.output_norm_gate(got["o"], ep["gate"], ep["weight"], eps=1e-6)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y.float()).all())
+    heads = [2, 50, 93]
+    ref = oracle.output_norm_gate(to64(got["o"][:, heads]), to64(ep["gate"][:, heads]),
+                                  to64(ep["weight"]), 1e-6)
+    g = to64(y[:, heads])
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-6 * float(np.sqrt(np.mean(ref * ref)))
+    excess = np.abs(g - ref) - bound
+    note("  epilogue: max |y - ref| / rms(ref) = %.3e" %
+         (float(np.max(np.abs(g - ref))) / float(np.sqrt(np.mean(ref * ref)))))
+    assert np.all(excess <= 0), "max excess %.3e" % float(np.max(excess))
+
+
+@pytest.mark.timeout(600)
 def test_varlen_workload():
     """8 packed sequences (32768 tokens), random h0 per sequence, conv reset per sequence."""
     run_prefill_workload("varlen", [7, 64])
