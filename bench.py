@@ -19,6 +19,8 @@ written).  ``value`` is prefill tokens/s.  The same JSON line carries:
   precomputed fp32 g, and that call's roofline;
 * ``output_epilogue``: the per-head RMSNorm and sigmoid output gate applied to the
   step's fp32 read-out (bf16 gate in, bf16 y out), timed alone, and its roofline;
+* ``decode_conv``: the same 256 decode steps from raw projections with the conv,
+  SiLU and q/k L2 fused in (kda_decode_step_conv; conv caches updated in place);
 * ``cpu_baseline``: the fp64 oracle (prologue + recurrence) timed on this host's
   cores over the same workload, repeated for at least ten seconds.
 
@@ -90,6 +92,42 @@ def gated_step_bytes(T: int, H: int, dk: int, dv: int, N: int, h0: bool) -> floa
     """As prefill_step_bytes with the gate's bf16 pre-activation z (2*dk per token and
     head) in place of the fp32 g; A_log and dt_bias are negligible."""
     return prefill_step_bytes(T, H, dk, dv, N, h0) - float(T * H * 2 * dk)
+
+
+def decode_conv_step_bytes(B: int, H: int, dk: int, dv: int) -> float:
+    """decode_step_bytes with raw q, k, v in place of the processed ones, plus the conv
+    caches read and written (3 bf16 tokens per channel) and the conv weights once."""
+    C = 2 * dk + dv
+    return float(decode_step_bytes(B, H, dk, dv) + B * H * 2 * 3 * C * 2 + H * C * 4 * 2)
+
+
+def run_decode_conv(torch, kda, workloads, steps=256, warmup=16):
+    spec = workloads.standard_specs()["decode"]
+    dev = "cuda:0"
+    B, H, DK, DV = spec.batch, spec.heads, spec.dk, spec.dv
+    state = workloads.make_decode_state(spec, dev)
+    cv = workloads.make_decode_conv(spec, dev)
+    ins = [workloads.make_decode_conv_step(spec, t, dev) for t in range(steps)]
+    o = torch.empty((B, H, DV), dtype=torch.float32, device=dev)
+
+    def call(d, st):
+        kda.decode_step_conv(d["q_raw"], d["k_raw"], d["v_raw"], cv["w_q"], cv["w_k"], cv["w_v"],
+                             cv["conv_q"], cv["conv_k"], cv["conv_v"], d["g"], d["beta"], st,
+                             out=o)
+
+    scratch = state.clone()
+    for t in range(warmup):
+        call(ins[t % steps], scratch)
+    del scratch
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for t in range(steps):
+        call(ins[t], state)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return dict(spec=spec, steps=steps, ms=a.elapsed_time(b), B=B, H=H, DK=DK, DV=DV)
 
 
 def epilogue_bytes(T: int, H: int, dv: int) -> float:
@@ -329,6 +367,19 @@ def main():
                                       "frac": round(dach / HBM_PEAK_GBS, 4),
                                       "traffic": measured_traffic("decode", "decode"),
                                       "algorithmic_bytes_per_launch": dbytes}}
+    if not args.no_decode:
+        d = run_decode_conv(torch, kda, workloads)
+        ms_dec = d["ms"] / d["steps"]
+        dbytes = decode_conv_step_bytes(d["B"], d["H"], d["DK"], d["DV"])
+        dach = dbytes / (ms_dec / 1e3) / 1e9
+        out["decode_conv"] = {"value": round(d["steps"] / (d["ms"] / 1e3), 1), "unit": "steps/s",
+                              "workload": d["spec"].name + ", conv+SiLU+L2 fused",
+                              "ms_per_step": round(ms_dec, 4),
+                              "roofline": {"bound": "hbm", "achieved": round(dach, 1),
+                                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                           "frac": round(dach / HBM_PEAK_GBS, 4),
+                                           "traffic": None,
+                                           "algorithmic_bytes_per_launch": dbytes}}
     if not args.no_gate:
         gres = run_prefill(args, torch, kda, workloads, gated=True)
         gbytes = gated_step_bytes(T, H, DK, DV, N, spec.h0_std is not None)

@@ -10,6 +10,7 @@ fallback: if libkda.so is missing the calls raise.
     chunk_fwd_gated(q, k, v, z, beta, ...)  -> (o, final_state)  the same, bounded gate fused
     output_norm_gate(o, gate, weight, ...)  -> y                 per-head RMSNorm * sigmoid gate
     decode_step(q, k, v, g, beta, state)    -> o                 one recurrent step
+    decode_step_conv(q_raw, ..., state)     -> o                 conv + SiLU + L2 + the step
 
 Build the library with ``python -m channel_gated_delta_amd.build``.
 """
@@ -22,7 +23,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["KdaError", "library", "short_conv", "chunk_fwd", "chunk_fwd_gated", "decode_step",
-           "output_norm_gate", "LIB_PATH"]
+           "output_norm_gate", "decode_step_conv", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -56,6 +57,9 @@ def library() -> ctypes.CDLL:
         lib.kda_chunk_fwd_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32,
                                             _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
                                             _vp, ctypes.c_size_t, _i32, _i32, _vp]
+        lib.kda_decode_step_conv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32,
+                                             _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp,
+                                             _i32, _i32, _vp]
         lib.kda_output_norm_gate.argtypes = [_vp, _vp, _vp, _f32, _i64, _i32, _i32, _i32, _vp,
                                              _vp]
         lib.kda_chunk_fwd_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -63,7 +67,8 @@ def library() -> ctypes.CDLL:
         lib.kda_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
                                         _vp, _i32, _i32, _vp]
         for fn in ("kda_short_conv", "kda_chunk_fwd", "kda_chunk_fwd_gated",
-                   "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_output_norm_gate"):
+                   "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_output_norm_gate",
+                   "kda_decode_step_conv"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_status_string.restype = ctypes.c_char_p
@@ -272,6 +277,48 @@ def chunk_workspace_bytes(total_tokens: int, num_heads: int, dk: int, dv: int,
                                                   int(dv), int(chunk_size), _DTYPES[dtype],
                                                   _DTYPES[out_dtype], ctypes.byref(n)))
     return int(n.value)
+
+
+def decode_step_conv(q_raw: torch.Tensor, k_raw: torch.Tensor, v_raw: torch.Tensor,
+                     w_q: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor,
+                     conv_q: torch.Tensor, conv_k: torch.Tensor, conv_v: torch.Tensor,
+                     g: torch.Tensor, beta: torch.Tensor, state: torch.Tensor, *,
+                     scale: Optional[float] = None, l2_eps: float = 1e-6,
+                     out: Optional[torch.Tensor] = None,
+                     out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """One generation step from raw projections: width-4 conv over the conv caches
+    (updated in place), SiLU, q/k L2, then the recurrent step (``state`` in place).
+
+    q_raw, k_raw: [B, H*dk]; v_raw: [B, H*dv]; w_*: [H*d, 4]; conv_*: [B, 3, H*d]
+    (all in the activation dtype); g: [B, H, dk]; beta: [B, H]; state fp32.
+    """
+    _dev(q_raw, "q_raw")
+    dt = q_raw.dtype
+    if dt not in _DTYPES:
+        raise ValueError("q_raw must be bf16 or fp32")
+    B, H, dk = g.shape
+    dv = state.shape[-1]
+    for t, name, d in ((q_raw, "q_raw", dk), (k_raw, "k_raw", dk), (v_raw, "v_raw", dv)):
+        _dev(t, name, dt, (B, H * d))
+    for t, name, d in ((w_q, "w_q", dk), (w_k, "w_k", dk), (w_v, "w_v", dv)):
+        _dev(t, name, dt, (H * d, 4))
+    for t, name, d in ((conv_q, "conv_q", dk), (conv_k, "conv_k", dk), (conv_v, "conv_v", dv)):
+        _dev(t, name, dt, (B, 3, H * d))
+    _dev(g, "g", torch.float32, (B, H, dk))
+    _dev(beta, "beta", torch.float32, (B, H))
+    _dev(state, "state", torch.float32, (B, H, dk, dv))
+    if out is not None:
+        out_dtype = out.dtype
+    if out_dtype not in _DTYPES:
+        raise ValueError("out_dtype must be bf16 or fp32")
+    o = out if out is not None else torch.empty((B, H, dv), dtype=out_dtype, device=g.device)
+    _dev(o, "out", out_dtype, (B, H, dv))
+    sc = dk ** -0.5 if scale is None else float(scale)
+    _check(library().kda_decode_step_conv(
+        _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(conv_q),
+        _ptr(conv_k), _ptr(conv_v), float(l2_eps), _ptr(g), _ptr(beta), _ptr(state), B, H, dk,
+        dv, sc, _ptr(o), _DTYPES[dt], _DTYPES[out_dtype], _stream(g)))
+    return o
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

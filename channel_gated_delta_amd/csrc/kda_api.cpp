@@ -261,9 +261,46 @@ KDA_API kda_status_t kda_decode_step(const void *q, const void *k, const void *v
     if ((int64_t)batch * num_heads > ((int64_t)1 << 31) - 1)
         return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: grid too large");
     kda::DecodeArgs a{q, k, v, g, beta, state, batch, num_heads, dk, dv, scale, o,
-                      out_dtype == KDA_DTYPE_F32};
+                      out_dtype == KDA_DTYPE_F32, false, {}};
     return from_hip(kda::launch_decode_step(a, dtype == KDA_DTYPE_BF16, (hipStream_t)stream),
                     "kda_decode_step");
+}
+
+KDA_API kda_status_t kda_decode_step_conv(const void *q_raw, const void *k_raw, const void *v_raw,
+                                          const void *w_q, const void *w_k, const void *w_v,
+                                          void *conv_q, void *conv_k, void *conv_v, float l2_eps,
+                                          const float *g, const float *beta, float *state,
+                                          int32_t batch, int32_t num_heads, int32_t dk, int32_t dv,
+                                          float scale, void *o, kda_dtype_t dtype,
+                                          kda_dtype_t out_dtype, void *stream) {
+    g_last_error[0] = '\0';
+    const char *who = "kda_decode_step_conv";
+    if (batch > 0 && (!q_raw || !k_raw || !v_raw || !w_q || !w_k || !w_v || !conv_q ||
+                      !conv_k || !conv_v || !g || !beta || !state || !o))
+        return fail(KDA_ERR_INVALID_ARG, "%s: NULL pointer", who);
+    if (batch < 0 || num_heads < 1) return fail(KDA_ERR_INVALID_ARG, "%s: bad sizes", who);
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype))
+        return fail(KDA_ERR_INVALID_ARG, "%s: bad dtype", who);
+    if (dtype == KDA_DTYPE_F32 && out_dtype != KDA_DTYPE_F32)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: fp32 inputs need an fp32 output", who);
+    if (!isfinite(scale)) return fail(KDA_ERR_INVALID_ARG, "%s: scale not finite", who);
+    if (!(l2_eps >= 0.f && isfinite(l2_eps)))
+        return fail(KDA_ERR_INVALID_ARG, "%s: l2_eps negative or not finite", who);
+    const void *ins[] = {q_raw, k_raw, v_raw, w_q, w_k, w_v, conv_q, conv_k, conv_v, g, beta,
+                         state};
+    for (const void *p : ins)
+        if (o && o == p) return fail(KDA_ERR_INVALID_ARG, "%s: o aliases an input", who);
+    if (batch > 0 && (conv_q == conv_k || conv_q == conv_v || conv_k == conv_v))
+        return fail(KDA_ERR_INVALID_ARG, "%s: the three conv caches must be distinct", who);
+    if (!head_dim_ok(dk) || !head_dim_ok(dv))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dk/dv not in {16,32,64,128}", who);
+    if ((int64_t)batch * num_heads > ((int64_t)1 << 31) - 1)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: grid too large", who);
+    kda::DecodeArgs a{nullptr, nullptr, nullptr, g, beta, state, batch, num_heads, dk, dv, scale,
+                      o, out_dtype == KDA_DTYPE_F32, true,
+                      kda::DecodeConvIn{q_raw, k_raw, v_raw, w_q, w_k, w_v, conv_q, conv_k,
+                                        conv_v, l2_eps, num_heads}};
+    return from_hip(kda::launch_decode_step(a, dtype == KDA_DTYPE_BF16, (hipStream_t)stream), who);
 }
 
 }  // extern "C"

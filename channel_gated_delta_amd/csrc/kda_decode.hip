@@ -18,6 +18,13 @@
 // A barrier-free layout with one wave per 32-column slice was slower (67%):
 // each of its loads touches eight rows 512 bytes apart.
 // The step is bound by HBM bandwidth (2 * dk * dv * 4 bytes per head).
+//
+// The conv variant (kda_decode_step_conv) runs the token's prologue in the same
+// workgroup first ([Walkthrough] 第二站: width-4 causal conv over the conv
+// cache, SiLU, then q and k scaled to unit length): one thread per channel of
+// q | k | v of the head computes its conv from the three cached inputs and this
+// token's raw projection, shifts the cache by one, and the L2 sums of squares
+// are reduced over the workgroup.  q, k and v stay in fp32 on chip.
 #include "kda_device.cuh"
 #include "kda_launch.h"
 
@@ -34,13 +41,52 @@ struct DecodeCfg {
     static_assert(kRowThreads * kRowsPerThread == DK, "row split");
 };
 
-template <class T, class TO, int DK, int DV>
+// Width-4 conv of one channel for the fused step.  conv_load reads the history
+// h0..h2 (oldest first), the current raw input and the weights (w[3] multiplies
+// the current input); conv_finish returns SiLU of the conv and shifts the cache
+// by one in place (this thread owns the channel).  The loads are issued before
+// the state loads, so the conv waits only for its own inputs.
+template <class T>
+struct ConvTap {
+    T x[4], w[4];   // h0, h1, h2, x_t and the channel's weights
+    T *cache;
+    size_t row;
+};
+template <class T>
+__device__ __forceinline__ void conv_load(ConvTap<T> &c, const T *__restrict__ x,
+                                          const T *__restrict__ w, T *cache, size_t row,
+                                          size_t ch) {
+    c.x[0] = cache[ch];
+    c.x[1] = cache[row + ch];
+    c.x[2] = cache[2 * row + ch];
+    c.x[3] = x[ch];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c.w[i] = w[ch * 4 + i];
+    c.cache = cache + ch;
+    c.row = row;
+}
+template <class T>
+__device__ __forceinline__ float conv_value(const ConvTap<T> &c) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc += to_f32(c.w[i]) * to_f32(c.x[i]);
+    return acc / (1.0f + expf(-acc));
+}
+template <class T>
+__device__ __forceinline__ void conv_shift(const ConvTap<T> &c) {
+    c.cache[0] = c.x[1];
+    c.cache[c.row] = c.x[2];
+    c.cache[2 * c.row] = c.x[3];
+}
+
+template <class T, class TO, int DK, int DV, bool CONV>
 __global__ __launch_bounds__(1024)
 void decode_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                    const float *__restrict__ g, const float *__restrict__ beta,
-                   float *__restrict__ state, float scale, TO *__restrict__ o) {
+                   float *__restrict__ state, float scale, TO *__restrict__ o, DecodeConvIn cv) {
     using Cfg = DecodeCfg<T, DK, DV>;
     constexpr int NT = Cfg::kThreads, RT = Cfg::kRowThreads, RPT = Cfg::kRowsPerThread;
+    static_assert(!CONV || 2 * DK + DV <= NT, "one thread per conv channel");
     __shared__ float s_ka[DK];        // a_c * k_c
     __shared__ float s_qa[DK];        // a_c * q_c
     __shared__ float s_a[DK];         // a_c
@@ -48,6 +94,8 @@ void decode_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     __shared__ float s_qk[NT / kWave + 1];
     __shared__ float s_red[2][RT][DV];
     __shared__ float s_be[DV];        // beta * e_j
+    __shared__ float s_x[CONV ? 2 * DK + DV : 1];       // conv + SiLU of q | k | v
+    __shared__ float s_ss[2][CONV ? NT / kWave + 1 : 1];  // sums of squares of q, k
 
     const int bh = blockIdx.x;        // (sequence, head) pair
     const int tid = threadIdx.x;
@@ -55,18 +103,79 @@ void decode_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     const int rg = tid / Cfg::kColThreads;
     float *S = state + (size_t)bh * DK * DV;
 
-    // Issue the state loads first: RPT float4 per thread, rows rg + i*RT.
+    // The per-head inputs: a thread owns key channel tid (threads DK and up load
+    // channel DK-1 again and use nothing), so the loads need no branch.
+    static_assert(NT >= DK, "one thread per key channel");
+    const size_t kc_off = (size_t)bh * DK + min(tid, DK - 1);
+    const float g_in = g[kc_off];
+    T q_in{}, k_in{};
+    if constexpr (!CONV) {
+        q_in = q[kc_off];
+        k_in = k[kc_off];
+    }
+
+    // Fused conv: this thread's channel of q | k | v.  Threads 2 DK + DV and up own
+    // none; they load the last v channel again and store nothing.  These loads are
+    // issued before the state's and need no branch, so the conv arithmetic waits
+    // only for them (the memory counter is in order) and overlaps the state's
+    // arrival; a branch would make the compiler wait for them at its end.
+    ConvTap<T> tap{};
+    const bool has_ch = CONV && tid < 2 * DK + DV;
+    const int which = tid >= 2 * DK ? 2 : tid / DK;   // 0: q, 1: k, 2: v
+    if constexpr (CONV) {
+        const int b = bh / cv.heads, h = bh % cv.heads;
+        const int D = which == 2 ? DV : DK;
+        const int c = which == 2 ? min(tid - 2 * DK, DV - 1) : tid % DK;
+        const size_t row = (size_t)cv.heads * D, ch = (size_t)h * D + c;
+        const T *x = static_cast<const T *>(which == 0 ? cv.xq : which == 1 ? cv.xk : cv.xv);
+        const T *w = static_cast<const T *>(which == 0 ? cv.wq : which == 1 ? cv.wk : cv.wv);
+        T *cache = static_cast<T *>(which == 0 ? cv.cq : which == 1 ? cv.ck : cv.cv);
+        conv_load(tap, x + (size_t)b * row, w, cache + (size_t)b * 3 * row, row, ch);
+    }
+
+    // Issue the state loads next: RPT float4 per thread, rows rg + i*RT.  Compiler
+    // barriers keep the conv loads above these and the conv arithmetic below.
+    asm volatile("" ::: "memory");
     f32x4 st[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
         st[i] = __builtin_nontemporal_load(
             reinterpret_cast<const f32x4 *>(S + (size_t)(rg + i * RT) * DV) + cg);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float inv_q = 1.f, inv_k = 1.f;
+    if constexpr (CONV) {
+        // every lane computes (lanes without a channel on a copy): the loads are then
+        // consumed on one straight path, and only the stores depend on the channel
+        const float y = conv_value(tap);
+        const float sq = has_ch && which == 0 ? y * y : 0.f;
+        const float sk = has_ch && which == 1 ? y * y : 0.f;
+        if (has_ch) {
+            s_x[tid] = y;
+            conv_shift(tap);
+        }
+        const float wsq = group_sum<kWave>(sq), wsk = group_sum<kWave>(sk);
+        if ((tid & (kWave - 1)) == 0) {
+            s_ss[0][tid / kWave] = wsq;
+            s_ss[1][tid / kWave] = wsk;
+        }
+        __syncthreads();
+        float nq = 0.f, nk = 0.f;
+#pragma unroll
+        for (int i = 0; i < (NT + kWave - 1) / kWave; ++i) {
+            nq += s_ss[0][i];
+            nk += s_ss[1][i];
+        }
+        inv_q = 1.0f / sqrtf(nq + cv.eps);
+        inv_k = 1.0f / sqrtf(nk + cv.eps);
+    }
 
     float qk_part = 0.f;
-    for (int c = tid; c < DK; c += NT) {
-        const float a = __expf(g[(size_t)bh * DK + c]);
-        const float kc = to_f32(k[(size_t)bh * DK + c]);
-        const float qc = to_f32(q[(size_t)bh * DK + c]);
+    if (tid < DK) {
+        const int c = tid;
+        const float a = __expf(g_in);
+        const float kc = CONV ? s_x[DK + c] * inv_k : to_f32(k_in);
+        const float qc = CONV ? s_x[c] * inv_q : to_f32(q_in);
         s_a[c] = a;
         s_k[c] = kc;
         s_ka[c] = a * kc;
@@ -103,7 +212,7 @@ void decode_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
 #pragma unroll
         for (int i = 0; i < (NT + kWave - 1) / kWave; ++i) qk += s_qk[i];
         const float b = beta[bh];
-        const float e = to_f32(v[(size_t)bh * DV + tid]) - p;
+        const float e = (CONV ? s_x[2 * DK + tid] : to_f32(v[(size_t)bh * DV + tid])) - p;
         s_be[tid] = b * e;
         o[(size_t)bh * DV + tid] = from_f32<TO>(scale * (r + b * e * qk));
     }
@@ -123,21 +232,27 @@ void decode_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     }
 }
 
+template <class T, int DK, int DV, bool CONV>
+hipError_t launch_conv_or_not(const DecodeArgs &a, hipStream_t s) {
+    const int blocks = a.batch * a.heads;
+    if (a.out_f32)
+        hipLaunchKernelGGL((decode_kernel<T, float, DK, DV, CONV>), dim3(blocks),
+                           dim3(DecodeCfg<T, DK, DV>::kThreads), 0, s,
+                           (const T *)a.q, (const T *)a.k, (const T *)a.v, a.g, a.beta, a.state,
+                           a.scale, (float *)a.o, a.conv);
+    else
+        hipLaunchKernelGGL((decode_kernel<T, T, DK, DV, CONV>), dim3(blocks),
+                           dim3(DecodeCfg<T, DK, DV>::kThreads), 0, s,
+                           (const T *)a.q, (const T *)a.k, (const T *)a.v, a.g, a.beta, a.state,
+                           a.scale, (T *)a.o, a.conv);
+    return hipGetLastError();
+}
+
 template <class T, int DK, int DV>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
-    const int blocks = a.batch * a.heads;
-    if (blocks == 0) return hipSuccess;
-    if (a.out_f32)
-        hipLaunchKernelGGL((decode_kernel<T, float, DK, DV>), dim3(blocks),
-                           dim3(DecodeCfg<T, DK, DV>::kThreads), 0, s,
-                           (const T *)a.q, (const T *)a.k, (const T *)a.v, a.g, a.beta, a.state,
-                           a.scale, (float *)a.o);
-    else
-        hipLaunchKernelGGL((decode_kernel<T, T, DK, DV>), dim3(blocks),
-                           dim3(DecodeCfg<T, DK, DV>::kThreads), 0, s,
-                           (const T *)a.q, (const T *)a.k, (const T *)a.v, a.g, a.beta, a.state,
-                           a.scale, (T *)a.o);
-    return hipGetLastError();
+    if (a.batch * a.heads == 0) return hipSuccess;
+    return a.with_conv ? launch_conv_or_not<T, DK, DV, true>(a, s)
+                       : launch_conv_or_not<T, DK, DV, false>(a, s);
 }
 
 template <class T, int DK>

@@ -51,14 +51,27 @@ struct NormGateArgs {
     void *y;
 };
 
+// Conv inputs of the fused decode step: this token's raw projections, the
+// width-4 conv weights and the conv caches (the last three raw inputs of every
+// sequence, oldest first; updated in place).
+struct DecodeConvIn {
+    const void *xq, *xk, *xv;   // [B, H*dk], [B, H*dk], [B, H*dv]
+    const void *wq, *wk, *wv;   // [H*dk, 4], [H*dk, 4], [H*dv, 4]
+    void *cq, *ck, *cv;         // [B, 3, H*dk], [B, 3, H*dk], [B, 3, H*dv]
+    float eps;                  // of the q / k L2 normalisation
+    int32_t heads;
+};
+
 struct DecodeArgs {
-    const void *q, *k, *v;
+    const void *q, *k, *v;      // unused with the conv
     const float *g, *beta;
     float *state;
     int32_t batch, heads, dk, dv;
     float scale;
     void *o;
     bool out_f32;   // o in fp32 (else in the input dtype)
+    bool with_conv;
+    DecodeConvIn conv;
 };
 
 // Each launcher returns hipSuccess, hipErrorNotSupported for a shape it has no

@@ -22,6 +22,9 @@ dtype; "N(0, s)" means standard deviation s):
   fp32 [H, D]
 * output-epilogue inputs (make_epilogue, seed + 2000): output-gate pre-activation
   N(0, 1) in the activation dtype [T, H, DV], norm weight 1 + N(0, 0.1) fp32 [DV]
+* decode with the conv (make_decode_conv, seed + 3000): conv weights N(0, 0.5) and
+  initial conv caches N(0, 1) (raw inputs) in the activation dtype; per step
+  (make_decode_conv_step) raw projections N(0, 1) and g, beta as above
 
 The pages' own workloads are a Kimi-K3 KDA layer: 96 heads of 128x128 state,
 width-4 short conv, gate floor -5; they publish no dataset or benchmark inputs.
@@ -169,6 +172,33 @@ def make_gate(spec: PrefillSpec, device="cpu") -> Dict[str, torch.Tensor]:
         "z": _normal((T, H, DK), gen, device, spec.gate_std).to(spec.dtype),
         "a_log": _normal((H,), gen, device, 0.3).float(),
         "dt_bias": _normal((H, DK), gen, device, 0.5).float(),
+    }
+
+
+def make_decode_conv(spec: DecodeSpec, device="cpu") -> Dict[str, torch.Tensor]:
+    """Conv weights ``w_q, w_k, w_v`` [H*D, 4] and initial conv caches ``conv_q,
+    conv_k, conv_v`` [B, 3, H*D] (the last three raw inputs) of a decode batch."""
+    gen = _gen(device, spec.seed + 3000)
+    B, H, DK, DV = spec.batch, spec.heads, spec.dk, spec.dv
+    out = {}
+    for name, D in (("q", DK), ("k", DK), ("v", DV)):
+        out["w_" + name] = _normal((H * D, 4), gen, device, 0.5).to(spec.dtype)
+    for name, D in (("q", DK), ("k", DK), ("v", DV)):
+        out["conv_" + name] = _normal((B, 3, H * D), gen, device).to(spec.dtype)
+    return out
+
+
+def make_decode_conv_step(spec: DecodeSpec, step: int, device="cpu") -> Dict[str, torch.Tensor]:
+    """Inputs of fused decode step ``step``: raw projections ``q_raw, k_raw`` [B, H*DK],
+    ``v_raw`` [B, H*DV] (before the conv), ``g`` [B, H, DK] and ``beta`` [B, H]."""
+    gen = _gen(device, (spec.seed + 3000) * 1_000_003 + 7919 * (step + 1))
+    B, H, DK, DV = spec.batch, spec.heads, spec.dk, spec.dv
+    return {
+        "q_raw": _normal((B, H * DK), gen, device).to(spec.dtype),
+        "k_raw": _normal((B, H * DK), gen, device).to(spec.dtype),
+        "v_raw": _normal((B, H * DV), gen, device).to(spec.dtype),
+        "g": (spec.gate_lb * torch.sigmoid(_normal((B, H, DK), gen, device))).float(),
+        "beta": torch.sigmoid(_normal((B, H), gen, device)).float(),
     }
 
 

@@ -219,6 +219,34 @@ KDA_API kda_status_t kda_decode_step(const void *q, const void *k, const void *v
                              kda_dtype_t out_dtype, void *stream);
 
 /*
+ * kda_decode_step_conv -- one generation step from this token's raw q/k/v
+ * projections: the prologue of kda_short_conv (width-4 causal conv over the
+ * conv cache, SiLU, q and k scaled to unit length; [Walkthrough] 第二站) and
+ * kda_decode_step's recurrent step, fused in one launch; q, k and v stay on
+ * chip in fp32 (they are not rounded to the activation dtype in between).
+ *
+ *   q_raw, k_raw  [batch, num_heads * dk]   dtype: this token's projections
+ *   v_raw         [batch, num_heads * dv]   dtype
+ *   w_q, w_k      [num_heads * dk, 4]       dtype (w[:, 3] multiplies the current token)
+ *   w_v           [num_heads * dv, 4]       dtype
+ *   conv_q, conv_k [batch, 3, num_heads * dk], conv_v [batch, 3, num_heads * dv]
+ *                 dtype: the last three raw inputs of every sequence (oldest
+ *                 first; the layout of kda_short_conv's conv_state), read and
+ *                 updated IN PLACE to end with this token; three distinct buffers.
+ *   l2_eps        the q / k normalisation's epsilon: u / sqrt(sum u^2 + l2_eps)
+ *   g, beta, state, scale, o: as kda_decode_step.
+ * No conv bias.  Supported: dk, dv in {16, 32, 64, 128}.  Cloning a sequence
+ * for branching is a device copy of its state and conv caches.
+ */
+KDA_API kda_status_t kda_decode_step_conv(const void *q_raw, const void *k_raw, const void *v_raw,
+                                          const void *w_q, const void *w_k, const void *w_v,
+                                          void *conv_q, void *conv_k, void *conv_v, float l2_eps,
+                                          const float *g, const float *beta, float *state,
+                                          int32_t batch, int32_t num_heads, int32_t dk, int32_t dv,
+                                          float scale, void *o, kda_dtype_t dtype,
+                                          kda_dtype_t out_dtype, void *stream);
+
+/*
  * kda_output_norm_gate -- the read-out's exit path before the output projection
  * ([Walkthrough] 第六站: a per-head RMSNorm, then the output gate scales each
  * channel).  For every row r (a (token, head) pair) of dv channels:

@@ -34,8 +34,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"kda_short_conv", "kda_chunk_fwd", "kda_chunk_fwd_gated",
                           "kda_chunk_fwd_workspace_size", "kda_decode_step",
-                          "kda_output_norm_gate", "kda_status_string", "kda_last_error",
-                          "kda_version"}
+                          "kda_output_norm_gate", "kda_decode_step_conv", "kda_status_string",
+                          "kda_last_error", "kda_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -206,6 +206,27 @@ def test_output_norm_gate_rejects(lib, kw, status):
     assert lib.kda_output_norm_gate(a["o"], a["gate"], a["w"], a["eps"], a["rows"], a["dv"],
                                     a["odt"], a["dt"], a["y"], NULL) == status
     assert b"kda_output_norm_gate" in lib.kda_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(xq=NULL), kda.KDA_ERR_INVALID_ARG),
+    (dict(cq=NULL), kda.KDA_ERR_INVALID_ARG),
+    (dict(cv=ctypes.c_void_p(4096 * 20)), kda.KDA_ERR_INVALID_ARG),   # conv_v is conv_q
+    (dict(o=ctypes.c_void_p(4096 * 20)), kda.KDA_ERR_INVALID_ARG),    # o aliases conv_q
+    (dict(eps=-1.0), kda.KDA_ERR_INVALID_ARG),
+    (dict(B=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(dk=8), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=F32, odt=BF16), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_decode_step_conv_rejects(lib, kw, status):
+    a = dict(xq=P, cq=ctypes.c_void_p(4096 * 20), cv=ctypes.c_void_p(4096 * 22), eps=1e-6, B=4,
+             dk=128, o=ctypes.c_void_p(8192), dtype=BF16, odt=F32)
+    a.update(kw)
+    assert lib.kda_decode_step_conv(
+        a["xq"], P, P, P, P, P, a["cq"], ctypes.c_void_p(4096 * 21), a["cv"], a["eps"], P, P,
+        ctypes.c_void_p(12288), a["B"], 2, a["dk"], 128, 0.1, a["o"], a["dtype"], a["odt"],
+        NULL) == status
+    assert b"kda_decode_step_conv" in lib.kda_last_error()
 
 
 def test_binding_refuses_cpu_tensors():

@@ -196,6 +196,82 @@ def test_gated_matches_plain_gate():
     assert_parity("state fused vs plain", to64(got["hT"]), to64(plain["hT"]), 1e-3)
 
 
+# ------------------------------------------------------------------ decode with the conv
+
+def decode_conv_case(B, H, dk, dv, steps, dtype, seed):
+    """`steps` fused steps against the oracle's prefill of the same tokens: the B
+    sequences packed, the initial conv caches as their conv history, the initial
+    states as h0 (q, k, v not rounded in between on either side)."""
+    spec = workloads.DecodeSpec("t", batch=B, heads=H, dk=dk, dv=dv, steps=steps, dtype=dtype,
+                                seed=seed)
+    state = workloads.make_decode_state(spec, DEV)
+    cv = workloads.make_decode_conv(spec, DEV)
+    s0 = state.clone()
+    c0 = {n: cv["conv_" + n].clone() for n in "qkv"}
+    ins, outs = [], []
+    for t in range(steps):
+        d = workloads.make_decode_conv_step(spec, t, DEV)
+        outs.append(kda.decode_step_conv(d["q_raw"], d["k_raw"], d["v_raw"], cv["w_q"], cv["w_k"],
+                                         cv["w_v"], cv["conv_q"], cv["conv_k"], cv["conv_v"],
+                                         d["g"], d["beta"], state, scale=dk ** -0.5))
+        ins.append(d)
+    torch.cuda.synchronize()
+
+    def packed(key):   # per-step [B, ...] -> sequence-major [B * steps, ...]
+        x = torch.stack([i[key] for i in ins], dim=1)
+        return to64(x.reshape(B * steps, *x.shape[2:]))
+
+    cu = np.arange(B + 1) * steps
+    q = oracle.prologue(packed("q_raw"), to64(cv["w_q"]), H, dk, cu, state_in=to64(c0["q"]),
+                        normalize=True)
+    k = oracle.prologue(packed("k_raw"), to64(cv["w_k"]), H, dk, cu, state_in=to64(c0["k"]),
+                        normalize=True)
+    v = oracle.prologue(packed("v_raw"), to64(cv["w_v"]), H, dv, cu, state_in=to64(c0["v"]))
+    o, hT = oracle.recurrent(q, k, v, packed("g"), packed("beta"), cu, dk ** -0.5, to64(s0))
+    tol = tol_for(dtype)
+    assert_parity("decode+conv o", to64(torch.stack(outs, dim=1).reshape(B * steps, H, dv)), o,
+                  tol)
+    assert_parity("decode+conv state", to64(state), hT, tol)
+    for n in "qkv":   # the caches end with the last three raw inputs, exactly
+        hist = torch.cat([c0[n], torch.stack([i[n + "_raw"] for i in ins], dim=1)], dim=1)[:, -3:]
+        assert torch.equal(cv["conv_" + n], hist), "conv cache " + n
+    return cv, state
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (16, 16), (32, 128), (128, 16), (64, 32)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_decode_conv(dk, dv, dtype):
+    note("decode+conv dk=%d dv=%d %s" % (dk, dv, dtype))
+    decode_conv_case(3, 2, dk, dv, 6, dtype, seed=dk + 3 * dv)
+
+
+def test_decode_conv_caches_match_short_conv():
+    """The fused step leaves exactly the conv caches kda_short_conv leaves for one token
+    per sequence.  (o and the state are checked against the oracle elsewhere: the
+    unfused pair rounds q, k, v to bf16 in between, which moves a single step's state
+    by ~2^-9 of its update -- about 9% of the state's rms for these inputs.)"""
+    B, H, dk, dv = 4, 3, 128, 64
+    spec = workloads.DecodeSpec("t", batch=B, heads=H, dk=dk, dv=dv, steps=1, seed=71)
+    cv = workloads.make_decode_conv(spec, DEV)
+    d = workloads.make_decode_conv_step(spec, 0, DEV)
+    st1 = workloads.make_decode_state(spec, DEV)
+    st2 = st1.clone()
+    caches = {n: cv["conv_" + n].clone() for n in "qkv"}
+    o1 = kda.decode_step_conv(d["q_raw"], d["k_raw"], d["v_raw"], cv["w_q"], cv["w_k"], cv["w_v"],
+                              cv["conv_q"], cv["conv_k"], cv["conv_v"], d["g"], d["beta"], st1)
+    cu = torch.arange(B + 1, dtype=torch.int32, device=DEV)
+    x = {}
+    for n, D in (("q", dk), ("k", dk), ("v", dv)):
+        x[n], caches[n] = kda.short_conv(d[n + "_raw"], cv["w_" + n], num_heads=H, head_dim=D,
+                                         cu_seqlens=cu, conv_state=caches[n],
+                                         output_final_state=True, l2_normalize=(n != "v"))
+    o2 = kda.decode_step(x["q"], x["k"], x["v"], d["g"], d["beta"], st2)
+    torch.cuda.synchronize()
+    for n in "qkv":
+        assert torch.equal(cv["conv_" + n], caches[n]), "conv cache " + n
+    assert bool(torch.isfinite(o1).all()) and bool(torch.isfinite(o2).all())
+
+
 # ------------------------------------------------------------------ output epilogue
 
 def check_norm_gate(o, gate, w, eps):

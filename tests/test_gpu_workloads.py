@@ -82,6 +82,43 @@ def test_prefill_workload_output_epilogue():
 
 
 @pytest.mark.timeout(600)
+def test_decode_conv_workload():
+    """64 sequences x 96 heads, 8 fused steps (conv + SiLU + L2 + the recurrent step) from
+    raw projections and conv caches; every (sequence, head) against the oracle."""
+    spec = workloads.standard_specs()["decode"]
+    B, H, DK, DV, steps = spec.batch, spec.heads, spec.dk, spec.dv, 8
+    note("decode+conv workload %d x %d heads, %d steps" % (B, H, steps))
+    state = workloads.make_decode_state(spec, DEV)
+    cv = workloads.make_decode_conv(spec, DEV)
+    s0 = to64(state)
+    c0 = {n: to64(cv["conv_" + n]) for n in "qkv"}
+    ins, outs = [], []
+    for t in range(steps):
+        d = workloads.make_decode_conv_step(spec, t, DEV)
+        outs.append(kda.decode_step_conv(d["q_raw"], d["k_raw"], d["v_raw"], cv["w_q"], cv["w_k"],
+                                         cv["w_v"], cv["conv_q"], cv["conv_k"], cv["conv_v"],
+                                         d["g"], d["beta"], state, scale=spec.dk ** -0.5))
+        ins.append({key: val.cpu() for key, val in d.items()})
+    torch.cuda.synchronize()
+    got_o = to64(torch.stack(outs, dim=1).reshape(B * steps, H, DV))
+    del outs
+
+    def packed(key):
+        x = torch.stack([i[key] for i in ins], dim=1)
+        return x.double().numpy().reshape(B * steps, *x.shape[2:])
+
+    cu = np.arange(B + 1) * steps
+    q = oracle.prologue(packed("q_raw"), to64(cv["w_q"]), H, DK, cu, state_in=c0["q"],
+                        normalize=True)
+    k = oracle.prologue(packed("k_raw"), to64(cv["w_k"]), H, DK, cu, state_in=c0["k"],
+                        normalize=True)
+    v = oracle.prologue(packed("v_raw"), to64(cv["w_v"]), H, DV, cu, state_in=c0["v"])
+    o, hT = oracle.recurrent(q, k, v, packed("g"), packed("beta"), cu, spec.dk ** -0.5, s0)
+    assert_parity("o (all pairs, all steps)", got_o, o, 2e-2)
+    assert_parity("final state", to64(state), hT, 2e-2)
+
+
+@pytest.mark.timeout(600)
 def test_varlen_workload():
     """8 packed sequences (32768 tokens), random h0 per sequence, conv reset per sequence."""
     run_prefill_workload("varlen", [7, 64])
