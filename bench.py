@@ -21,6 +21,8 @@ written).  ``value`` is prefill tokens/s.  The same JSON line carries:
   step's fp32 read-out (bf16 gate in, bf16 y out), timed alone, and its roofline;
 * ``decode_conv``: the same 256 decode steps from raw projections with the conv,
   SiLU and q/k L2 fused in (kda_decode_step_conv; conv caches updated in place);
+* ``gdn``: the prefill step with one decay per (token, head) (kda_gdn_chunk_fwd,
+  g [T, H]) and that call's roofline;
 * ``cpu_baseline``: the fp64 oracle (prologue + recurrence) timed on this host's
   cores over the same workload, repeated for at least ten seconds.
 
@@ -47,9 +49,12 @@ KERNEL_SOURCES = {
     "chunk": ("kda_device.cuh", "kda_chunk_common.cuh", "kda_chunk_prep.cuh", "kda_chunk_state.cuh",
               "kda_chunk_dispatch.cuh", "kda_chunk_bf16.hip"),
     "decode": ("kda_device.cuh", "kda_decode.hip"),
+    "decodeconv": ("kda_device.cuh", "kda_decode.hip"),
     "gated": ("kda_device.cuh", "kda_chunk_common.cuh", "kda_chunk_prep.cuh",
               "kda_chunk_state.cuh", "kda_chunk_dispatch.cuh", "kda_chunk_bf16_gz.hip"),
     "epilogue": ("kda_device.cuh", "kda_epilogue.hip"),
+    "gdn": ("kda_device.cuh", "kda_chunk_common.cuh", "kda_chunk_prep.cuh",
+            "kda_chunk_state.cuh", "kda_chunk_dispatch.cuh", "kda_chunk_bf16_gdn.hip"),
 }
 
 
@@ -86,6 +91,11 @@ def prefill_step_bytes(T: int, H: int, dk: int, dv: int, N: int, h0: bool) -> fl
     per_tok_head = 2 * dk + 2 * dk + 2 * dv + 4 * dk + 4 + 4 * dv
     states = N * H * dk * dv * 4 * (2 if h0 else 1)
     return float(T * H * per_tok_head + states)
+
+
+def gdn_step_bytes(T: int, H: int, dk: int, dv: int, N: int, h0: bool) -> float:
+    """As prefill_step_bytes with one fp32 decay per (token, head) in place of g."""
+    return prefill_step_bytes(T, H, dk, dv, N, h0) - float(T * H * (4 * dk - 4))
 
 
 def gated_step_bytes(T: int, H: int, dk: int, dv: int, N: int, h0: bool) -> float:
@@ -162,12 +172,13 @@ def decode_step_bytes(B: int, H: int, dk: int, dv: int) -> float:
     return float(B * H * (2 * dk * dv * 4 + 2 * dk * 2 + dv * 2 + 4 * dk + 4 + 4 * dv))
 
 
-def run_prefill(args, torch, kda, workloads, gated=False):
+def run_prefill(args, torch, kda, workloads, gated=False, gdn=False):
     specs = workloads.standard_specs()
     spec = specs[args.workload]
     dev = "cuda:0"
     inp = workloads.make_prefill(spec, dev)
     gate = workloads.make_gate(spec, dev) if gated else None
+    ghead = workloads.make_head_gate(spec, dev) if gdn else None
     H, DK, DV = spec.heads, spec.dk, spec.dv
     T, N = spec.total_tokens, len(spec.lengths)
     cu = inp["cu_seqlens"] if N > 1 else None
@@ -188,7 +199,12 @@ def run_prefill(args, torch, kda, workloads, gated=False):
         kda.short_conv(inp["v_raw"], inp["w_v"], num_heads=H, head_dim=DV, cu_seqlens=cu, out=vb)
         if ev is not None:
             ev[0].record(stream)
-        if gate is None:
+        if ghead is not None:
+            kda.gdn_chunk_fwd(qb, kb, vb, ghead, inp["beta"], cu_seqlens=cu,
+                              scale=spec.read_scale, gate_lower_bound=spec.gate_lb,
+                              chunk_size=spec.chunk, initial_state=inp["h0"], out=ob,
+                              final_state=hT, workspace=ws)
+        elif gate is None:
             kda.chunk_fwd(qb, kb, vb, inp["g"], inp["beta"], cu_seqlens=cu,
                           scale=spec.read_scale, gate_lower_bound=spec.gate_lb,
                           chunk_size=spec.chunk, initial_state=inp["h0"], out=ob, final_state=hT,
@@ -378,7 +394,7 @@ def main():
                               "roofline": {"bound": "hbm", "achieved": round(dach, 1),
                                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                            "frac": round(dach / HBM_PEAK_GBS, 4),
-                                           "traffic": None,
+                                           "traffic": measured_traffic("decodeconv", "decode"),
                                            "algorithmic_bytes_per_launch": dbytes}}
     if not args.no_gate:
         gres = run_prefill(args, torch, kda, workloads, gated=True)
@@ -395,6 +411,21 @@ def main():
                          "kernel": "kda_chunk_fwd_gated", "algorithmic_bytes_per_launch": gbytes,
                          "avg_launch_ms": round(gres["chunk_ms"], 4)}}
         del gres
+    if not args.no_gate:
+        hres = run_prefill(args, torch, kda, workloads, gdn=True)
+        hbytes = gdn_step_bytes(T, H, DK, DV, N, spec.h0_std is not None)
+        hach = hbytes / (hres["chunk_ms"] / 1e3) / 1e9
+        out["gdn"] = {
+            "value": round(T / (hres["ms_step"] / 1e3), 1), "unit": "tokens/s",
+            "ms_per_step": round(hres["ms_step"], 4),
+            "path": "3x short_conv + gdn_chunk_fwd (one decay per token and head)",
+            "roofline": {"bound": "hbm", "achieved": round(hach, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(hach / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("gdn", args.workload),
+                         "kernel": "kda_gdn_chunk_fwd",
+                         "algorithmic_bytes_per_launch": hbytes,
+                         "avg_launch_ms": round(hres["chunk_ms"], 4)}}
+        del hres
     if not args.no_epilogue:
         ems = run_epilogue(args, torch, kda, workloads, res["o"])
         ebytes = epilogue_bytes(T, H, DV)

@@ -9,6 +9,7 @@ fallback: if libkda.so is missing the calls raise.
     chunk_fwd(q, k, v, g, beta, ...)        -> (o, final_state)  chunkwise prefill
     chunk_fwd_gated(q, k, v, z, beta, ...)  -> (o, final_state)  the same, bounded gate fused
     output_norm_gate(o, gate, weight, ...)  -> y                 per-head RMSNorm * sigmoid gate
+    gdn_chunk_fwd / gdn_decode_step         one decay per (token, head): g [T, H] / [B, H]
     decode_step(q, k, v, g, beta, state)    -> o                 one recurrent step
     decode_step_conv(q_raw, ..., state)     -> o                 conv + SiLU + L2 + the step
 
@@ -23,7 +24,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["KdaError", "library", "short_conv", "chunk_fwd", "chunk_fwd_gated", "decode_step",
-           "output_norm_gate", "decode_step_conv", "LIB_PATH"]
+           "output_norm_gate", "decode_step_conv", "gdn_chunk_fwd", "gdn_decode_step",
+           "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -66,9 +68,11 @@ def library() -> ctypes.CDLL:
                                                      ctypes.POINTER(ctypes.c_size_t)]
         lib.kda_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
                                         _vp, _i32, _i32, _vp]
+        lib.kda_gdn_chunk_fwd.argtypes = lib.kda_chunk_fwd.argtypes
+        lib.kda_gdn_decode_step.argtypes = lib.kda_decode_step.argtypes
         for fn in ("kda_short_conv", "kda_chunk_fwd", "kda_chunk_fwd_gated",
                    "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_output_norm_gate",
-                   "kda_decode_step_conv"):
+                   "kda_decode_step_conv", "kda_gdn_chunk_fwd", "kda_gdn_decode_step"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_status_string.restype = ctypes.c_char_p
@@ -175,6 +179,22 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
                   initial_state, output_final_state, out, final_state, out_dtype, workspace)
 
 
+def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, *, cu_seqlens: Optional[torch.Tensor] = None,
+                  scale: Optional[float] = None, gate_lower_bound: float = -5.0,
+                  chunk_size: int = 64, initial_state: Optional[torch.Tensor] = None,
+                  output_final_state: bool = True, out: Optional[torch.Tensor] = None,
+                  final_state: Optional[torch.Tensor] = None,
+                  out_dtype: torch.dtype = torch.float32,
+                  workspace: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``chunk_fwd`` with one decay per (token, head): g [T, H] fp32 (GDN's gate)."""
+    T, H, dk = q.shape
+    _dev(g, "g", torch.float32, (T, H))
+    return _chunk(q, k, v, g, "head", beta, cu_seqlens, scale, gate_lower_bound, chunk_size,
+                  initial_state, output_final_state, out, final_state, out_dtype, workspace)
+
+
 def chunk_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, z: torch.Tensor,
                     beta: torch.Tensor, *, a_log: Optional[torch.Tensor] = None,
                     dt_bias: Optional[torch.Tensor] = None, lower_bound: float = -5.0,
@@ -229,8 +249,9 @@ def _chunk(q, k, v, g, gate, beta, cu_seqlens, scale, lower_bound, chunk_size, i
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace", torch.uint8)
-    if gate is None:
-        _check(library().kda_chunk_fwd(
+    if gate is None or gate == "head":
+        fn = library().kda_chunk_fwd if gate is None else library().kda_gdn_chunk_fwd
+        _check(fn(
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,
             int(chunk_size), sc, float(lower_bound), _ptr(initial_state), _ptr(final_state),
             _ptr(o), _ptr(workspace), workspace.numel(), _DTYPES[dt], _DTYPES[out_dtype],
@@ -321,10 +342,19 @@ def decode_step_conv(q_raw: torch.Tensor, k_raw: torch.Tensor, v_raw: torch.Tens
     return o
 
 
+def gdn_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, state: torch.Tensor, *, scale: Optional[float] = None,
+                    out: Optional[torch.Tensor] = None,
+                    out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """``decode_step`` with one decay per (sequence, head): g [B, H] fp32 (GDN's gate)."""
+    return decode_step(q, k, v, g, beta, state, scale=scale, out=out, out_dtype=out_dtype,
+                       _head_gate=True)
+
+
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                 beta: torch.Tensor, state: torch.Tensor, *, scale: Optional[float] = None,
                 out: Optional[torch.Tensor] = None,
-                out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+                out_dtype: torch.dtype = torch.float32, _head_gate: bool = False) -> torch.Tensor:
     """One recurrent step; ``state`` [B, H, dk, dv] fp32 is updated in place.
 
     q, k, g: [B, H, dk]; v: [B, H, dv]; beta: [B, H].  Returns o [B, H, dv]
@@ -338,7 +368,7 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     dv = v.shape[-1]
     _dev(k, "k", dt, (B, H, dk))
     _dev(v, "v", dt, (B, H, dv))
-    _dev(g, "g", torch.float32, (B, H, dk))
+    _dev(g, "g", torch.float32, (B, H) if _head_gate else (B, H, dk))
     _dev(beta, "beta", torch.float32, (B, H))
     _dev(state, "state", torch.float32, (B, H, dk, dv))
     if out is not None:
@@ -348,7 +378,8 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     o = out if out is not None else torch.empty((B, H, dv), dtype=out_dtype, device=q.device)
     _dev(o, "out", out_dtype, (B, H, dv))
     sc = dk ** -0.5 if scale is None else float(scale)
-    _check(library().kda_decode_step(
+    fn = library().kda_gdn_decode_step if _head_gate else library().kda_decode_step
+    _check(fn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), B, H, dk, dv, sc, _ptr(o),
         _DTYPES[dt], _DTYPES[out_dtype], _stream(q)))
     return o

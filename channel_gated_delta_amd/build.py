@@ -23,7 +23,8 @@ ARCH = "gfx950"
 
 SOURCES = ["kda_api.cpp", "kda_prologue.hip", "kda_decode.hip", "kda_chunk_bf16.hip",
            "kda_chunk_bf16_bf16out.hip", "kda_chunk_f32.hip", "kda_chunk_bf16_gz.hip",
-           "kda_chunk_bf16_bf16out_gz.hip", "kda_chunk_f32_gz.hip", "kda_epilogue.hip"]
+           "kda_chunk_bf16_bf16out_gz.hip", "kda_chunk_f32_gz.hip", "kda_epilogue.hip",
+           "kda_chunk_bf16_gdn.hip", "kda_chunk_bf16_bf16out_gdn.hip", "kda_chunk_f32_gdn.hip"]
 
 # Packed-fp32 instructions are disabled for device code: hipcc -O3 would emit
 # v_pk_{add,mul,fma}_f32 from plain float code otherwise.

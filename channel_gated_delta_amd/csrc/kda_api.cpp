@@ -33,8 +33,13 @@ int vec_elems(kda_dtype_t) { return 4; }   // channels per lane of the conv kern
 
 namespace {
 
-kda::ChunkLauncher chunk_launcher(kda_dtype_t dtype, kda_dtype_t out_dtype, bool gated = false) {
-    if (gated)
+// gate: 0 = g [T, H, dk], 1 = the fused bounded gate, 2 = g [T, H] (one decay per head)
+kda::ChunkLauncher chunk_launcher(kda_dtype_t dtype, kda_dtype_t out_dtype, int gate = 0) {
+    if (gate == 2)
+        return dtype == KDA_DTYPE_F32       ? kda::launch_chunk_f32_gdn
+               : out_dtype == KDA_DTYPE_F32 ? kda::launch_chunk_bf16_f32out_gdn
+                                            : kda::launch_chunk_bf16_bf16out_gdn;
+    if (gate == 1)
         return dtype == KDA_DTYPE_F32       ? kda::launch_chunk_f32_gz
                : out_dtype == KDA_DTYPE_F32 ? kda::launch_chunk_bf16_f32out_gz
                                             : kda::launch_chunk_bf16_bf16out_gz;
@@ -80,11 +85,13 @@ int chunk_shape_check(const char *who, int64_t total_tokens, int32_t num_heads, 
     return c;
 }
 
-// The checks and the launch shared by kda_chunk_fwd and kda_chunk_fwd_gated;
-// `gate` is g or the gate's pre-activation z.
+// The checks and the launch shared by kda_chunk_fwd, kda_chunk_fwd_gated and
+// kda_gdn_chunk_fwd; `gate` is g, the gate's pre-activation z, or the per-head g
+// (mode 0, 1, 2 as for chunk_launcher).
 kda_status_t chunk_checked_launch(const char *who, const kda::ChunkArgs &a, const void *gate,
-                                  bool gated, size_t workspace_bytes, kda_dtype_t dtype,
+                                  int mode, size_t workspace_bytes, kda_dtype_t dtype,
                                   kda_dtype_t out_dtype, void *stream) {
+    const bool gated = mode == 1;
     if (a.total_tokens > 0 &&
         (!a.q || !a.k || !a.v || !gate || !a.beta || !a.o || !a.workspace))
         return fail(KDA_ERR_INVALID_ARG, "%s: NULL q/k/v/%s/beta/o/workspace", who,
@@ -110,8 +117,33 @@ kda_status_t chunk_checked_launch(const char *who, const kda::ChunkArgs &a, cons
         return fail(KDA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", who,
                     workspace_bytes, kda::chunk_workspace_bytes(a.total_tokens, a.heads, c));
     int used = 0;
-    return from_hip(chunk_launcher(dtype, out_dtype, gated)(a, (hipStream_t)stream, true, &used),
+    return from_hip(chunk_launcher(dtype, out_dtype, mode)(a, (hipStream_t)stream, true, &used),
                     who);
+}
+
+kda_status_t decode_checked(const char *who, const void *q, const void *k, const void *v,
+                            const float *g, const float *beta, float *state, int32_t batch,
+                            int32_t num_heads, int32_t dk, int32_t dv, float scale, void *o,
+                            kda_dtype_t dtype, kda_dtype_t out_dtype, bool head_gate,
+                            void *stream) {
+    if (batch > 0 && (!q || !k || !v || !g || !beta || !state || !o))
+        return fail(KDA_ERR_INVALID_ARG, "%s: NULL pointer", who);
+    if (batch < 0 || num_heads < 1) return fail(KDA_ERR_INVALID_ARG, "%s: bad sizes", who);
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype))
+        return fail(KDA_ERR_INVALID_ARG, "%s: bad dtype", who);
+    if (dtype == KDA_DTYPE_F32 && out_dtype != KDA_DTYPE_F32)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: fp32 inputs need an fp32 output", who);
+    if (!isfinite(scale)) return fail(KDA_ERR_INVALID_ARG, "%s: scale not finite", who);
+    if (o && (o == q || o == k || o == v || o == (const void *)g || o == (const void *)beta ||
+              o == (const void *)state))
+        return fail(KDA_ERR_INVALID_ARG, "%s: o aliases an input", who);
+    if (!head_dim_ok(dk) || !head_dim_ok(dv))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dk/dv not in {16,32,64,128}", who);
+    if ((int64_t)batch * num_heads > ((int64_t)1 << 31) - 1)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: grid too large", who);
+    kda::DecodeArgs a{q, k, v, g, beta, state, batch, num_heads, dk, dv, scale, o,
+                      out_dtype == KDA_DTYPE_F32, false, {}, head_gate};
+    return from_hip(kda::launch_decode_step(a, dtype == KDA_DTYPE_BF16, (hipStream_t)stream), who);
 }
 
 }  // namespace
@@ -191,7 +223,23 @@ KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, 
     const kda::ChunkArgs a{q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, dk,
                            dv, chunk_size, scale, gate_lower_bound, initial_state, final_state, o,
                            (float *)workspace, nullptr, nullptr, nullptr};
-    return chunk_checked_launch("kda_chunk_fwd", a, g, false, workspace_bytes, dtype, out_dtype,
+    return chunk_checked_launch("kda_chunk_fwd", a, g, 0, workspace_bytes, dtype, out_dtype,
+                                stream);
+}
+
+KDA_API kda_status_t kda_gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                                       const float *beta, const int32_t *cu_seqlens,
+                                       int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                       int32_t dk, int32_t dv, int32_t chunk_size, float scale,
+                                       float gate_lower_bound, const float *initial_state,
+                                       float *final_state, void *o, void *workspace,
+                                       size_t workspace_bytes, kda_dtype_t dtype,
+                                       kda_dtype_t out_dtype, void *stream) {
+    g_last_error[0] = '\0';
+    const kda::ChunkArgs a{q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, dk,
+                           dv, chunk_size, scale, gate_lower_bound, initial_state, final_state, o,
+                           (float *)workspace, nullptr, nullptr, nullptr};
+    return chunk_checked_launch("kda_gdn_chunk_fwd", a, g, 2, workspace_bytes, dtype, out_dtype,
                                 stream);
 }
 
@@ -208,7 +256,7 @@ KDA_API kda_status_t kda_chunk_fwd_gated(const void *q, const void *k, const voi
     const kda::ChunkArgs a{q, k, v, nullptr, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
                            dk, dv, chunk_size, scale, lower_bound, initial_state, final_state, o,
                            (float *)workspace, z, a_log, dt_bias};
-    return chunk_checked_launch("kda_chunk_fwd_gated", a, z, true, workspace_bytes, dtype,
+    return chunk_checked_launch("kda_chunk_fwd_gated", a, z, 1, workspace_bytes, dtype,
                                 out_dtype, stream);
 }
 
@@ -245,25 +293,18 @@ KDA_API kda_status_t kda_decode_step(const void *q, const void *k, const void *v
                                      void *o, kda_dtype_t dtype, kda_dtype_t out_dtype,
                                      void *stream) {
     g_last_error[0] = '\0';
-    if (batch > 0 && (!q || !k || !v || !g || !beta || !state || !o))
-        return fail(KDA_ERR_INVALID_ARG, "kda_decode_step: NULL pointer");
-    if (batch < 0 || num_heads < 1) return fail(KDA_ERR_INVALID_ARG, "kda_decode_step: bad sizes");
-    if (!valid_dtype(dtype) || !valid_dtype(out_dtype))
-        return fail(KDA_ERR_INVALID_ARG, "kda_decode_step: bad dtype");
-    if (dtype == KDA_DTYPE_F32 && out_dtype != KDA_DTYPE_F32)
-        return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: fp32 inputs need an fp32 output");
-    if (!isfinite(scale)) return fail(KDA_ERR_INVALID_ARG, "kda_decode_step: scale not finite");
-    if (o && (o == q || o == k || o == v || o == (const void *)g || o == (const void *)beta ||
-              o == (const void *)state))
-        return fail(KDA_ERR_INVALID_ARG, "kda_decode_step: o aliases an input");
-    if (!head_dim_ok(dk) || !head_dim_ok(dv))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: dk/dv not in {16,32,64,128}");
-    if ((int64_t)batch * num_heads > ((int64_t)1 << 31) - 1)
-        return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: grid too large");
-    kda::DecodeArgs a{q, k, v, g, beta, state, batch, num_heads, dk, dv, scale, o,
-                      out_dtype == KDA_DTYPE_F32, false, {}};
-    return from_hip(kda::launch_decode_step(a, dtype == KDA_DTYPE_BF16, (hipStream_t)stream),
-                    "kda_decode_step");
+    return decode_checked("kda_decode_step", q, k, v, g, beta, state, batch, num_heads, dk, dv,
+                          scale, o, dtype, out_dtype, false, stream);
+}
+
+KDA_API kda_status_t kda_gdn_decode_step(const void *q, const void *k, const void *v,
+                                         const float *g, const float *beta, float *state,
+                                         int32_t batch, int32_t num_heads, int32_t dk, int32_t dv,
+                                         float scale, void *o, kda_dtype_t dtype,
+                                         kda_dtype_t out_dtype, void *stream) {
+    g_last_error[0] = '\0';
+    return decode_checked("kda_gdn_decode_step", q, k, v, g, beta, state, batch, num_heads, dk,
+                          dv, scale, o, dtype, out_dtype, true, stream);
 }
 
 KDA_API kda_status_t kda_decode_step_conv(const void *q_raw, const void *k_raw, const void *v_raw,
@@ -299,7 +340,8 @@ KDA_API kda_status_t kda_decode_step_conv(const void *q_raw, const void *k_raw, 
     kda::DecodeArgs a{nullptr, nullptr, nullptr, g, beta, state, batch, num_heads, dk, dv, scale,
                       o, out_dtype == KDA_DTYPE_F32, true,
                       kda::DecodeConvIn{q_raw, k_raw, v_raw, w_q, w_k, w_v, conv_q, conv_k,
-                                        conv_v, l2_eps, num_heads}};
+                                        conv_v, l2_eps, num_heads},
+                      false};
     return from_hip(kda::launch_decode_step(a, dtype == KDA_DTYPE_BF16, (hipStream_t)stream), who);
 }
 

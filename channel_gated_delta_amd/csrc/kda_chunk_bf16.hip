@@ -4,6 +4,6 @@
 
 namespace kda {
 hipError_t launch_chunk_bf16_f32out(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used) {
-    return chunk_detail::dispatch<bf16, float, false>(a, s, launch, chunk_used);
+    return chunk_detail::dispatch<bf16, float, kGatePlain>(a, s, launch, chunk_used);
 }
 }  // namespace kda

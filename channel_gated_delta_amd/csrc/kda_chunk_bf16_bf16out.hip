@@ -3,6 +3,6 @@
 
 namespace kda {
 hipError_t launch_chunk_bf16_bf16out(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used) {
-    return chunk_detail::dispatch<bf16, bf16, false>(a, s, launch, chunk_used);
+    return chunk_detail::dispatch<bf16, bf16, kGatePlain>(a, s, launch, chunk_used);
 }
 }  // namespace kda

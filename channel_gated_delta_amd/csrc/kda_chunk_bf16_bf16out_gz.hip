@@ -4,6 +4,6 @@
 
 namespace kda {
 hipError_t launch_chunk_bf16_bf16out_gz(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used) {
-    return chunk_detail::dispatch<bf16, bf16, true>(a, s, launch, chunk_used);
+    return chunk_detail::dispatch<bf16, bf16, kGateFused>(a, s, launch, chunk_used);
 }
 }  // namespace kda

@@ -51,15 +51,20 @@ __device__ __forceinline__ void st_off(void *base, uint32_t byte_off, V x) {
     *reinterpret_cast<V *>(reinterpret_cast<char *>(base) + byte_off) = x;
 }
 
-// Source of the log-decay g of every (token, head, key channel).  Plain: read
-// from g [T, H, dk] (fp32).  Fused bounded gate ([Walkthrough] 彩蛋: the gate
-// function with a lower bound): formed from the gate's pre-activation z
-// [T, H, dk] (activation dtype), a per-head A_log and a per-channel bias as
-//     g = lb * sigmoid(e^{A_log[h]} (z + dt_bias[h, c])),
-// so lb <= g <= 0 by construction.  The kernels take the source by value and a
-// compile-time switch GZ (true: the fused gate) telling which fields they read.
+// Source of the log-decay g of every (token, head, key channel), chosen by the
+// kernels' compile-time gate mode GM:
+//  * kGatePlain: read from g [T, H, dk] (fp32);
+//  * kGateFused: the bounded gate ([Walkthrough] 彩蛋: the gate function with a
+//    lower bound) formed from its pre-activation z [T, H, dk] (activation dtype),
+//    a per-head A_log and a per-channel bias as
+//        g = lb * sigmoid(e^{A_log[h]} (z + dt_bias[h, c])),
+//    so lb <= g <= 0 by construction;
+//  * kGateHead: one decay per (token, head), g [T, H] (fp32), the same for every
+//    key channel -- the head-wise forget gate of GDN, the coarser variant the
+//    pages compare KDA with ([Replication-1]).
+enum { kGatePlain = 0, kGateFused = 1, kGateHead = 2 };
 struct GateSrc {
-    const float *g;        // plain gate
+    const float *g;        // plain gate [T, H, dk], or the per-head gate [T, H]
     const void *z;         // fused gate: pre-activation
     const float *a_log;    // [H], NULL = 0
     const float *dt_bias;  // [H, dk], NULL = 0

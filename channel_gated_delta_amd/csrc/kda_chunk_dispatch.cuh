@@ -40,7 +40,7 @@ int pick_chunk(int chunk) {
     return 0;
 }
 
-template <class T, class TO, int DK, int BV, int C, bool GZ>
+template <class T, class TO, int DK, int BV, int C, int GM>
 hipError_t run(const ChunkArgs &a, hipStream_t s) {
     if constexpr (!fits<T, DK, BV, C>()) {
         return hipErrorNotSupported;
@@ -53,13 +53,13 @@ hipError_t run(const ChunkArgs &a, hipStream_t s) {
             if constexpr (std::is_same<T, bf16>::value && C == 16 && DK % 32 == 0) {
                 // one wave per (tile, head), four per workgroup
                 const int64_t units = ntiles * a.heads;
-                hipLaunchKernelGGL((chunk_prep16_kernel<DK, GZ>), dim3((unsigned)((units + 3) / 4)),
+                hipLaunchKernelGGL((chunk_prep16_kernel<DK, GM>), dim3((unsigned)((units + 3) / 4)),
                                    dim3(256), 0, s, (const bf16 *)a.q, (const bf16 *)a.k, gs,
                                    a.beta, a.cu_seqlens, a.num_seqs, a.total_tokens, a.heads,
                                    a.scale, units, tb, pm);
             } else {
                 const dim3 g1((unsigned)ntiles, (unsigned)a.heads);
-                hipLaunchKernelGGL((chunk_prep_kernel<T, DK, C, GZ>), g1, dim3(256), 0, s,
+                hipLaunchKernelGGL((chunk_prep_kernel<T, DK, C, GM>), g1, dim3(256), 0, s,
                                    (const T *)a.q, (const T *)a.k, gs, a.beta, a.cu_seqlens,
                                    a.num_seqs, a.total_tokens, a.heads, a.scale, tb, pm);
             }
@@ -70,7 +70,7 @@ hipError_t run(const ChunkArgs &a, hipStream_t s) {
         const int units = a.num_seqs * a.heads;
         const int nslice = a.dv / BV;
         const unsigned g2 = (unsigned)(((units + 7) / 8) * 8 * nslice);
-        hipLaunchKernelGGL((chunk_state_kernel<T, TO, DK, BV, C, GZ>), dim3(g2),
+        hipLaunchKernelGGL((chunk_state_kernel<T, TO, DK, BV, C, GM>), dim3(g2),
                            dim3(StateCfg<T, DK, BV, C>::NT), 0, s,
                            (const T *)a.q, (const T *)a.k, (const T *)a.v, gs, tb, pm,
                            a.cu_seqlens, a.total_tokens, a.heads, a.dv, a.scale, a.h0, a.hT,
@@ -79,16 +79,16 @@ hipError_t run(const ChunkArgs &a, hipStream_t s) {
     }
 }
 
-template <class T, class TO, int DK, int C, bool GZ>
+template <class T, class TO, int DK, int C, int GM>
 hipError_t run_bv(const ChunkArgs &a, hipStream_t s) {
     switch (pick_bv(a.dv)) {
-        case 64: return run<T, TO, DK, 64, C, GZ>(a, s);
-        case 32: return run<T, TO, DK, 32, C, GZ>(a, s);
-        default: return run<T, TO, DK, 16, C, GZ>(a, s);
+        case 64: return run<T, TO, DK, 64, C, GM>(a, s);
+        case 32: return run<T, TO, DK, 32, C, GM>(a, s);
+        default: return run<T, TO, DK, 16, C, GM>(a, s);
     }
 }
 
-template <class T, class TO, int DK, bool GZ>
+template <class T, class TO, int DK, int GM>
 hipError_t run_dk(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used) {
     const int c = pick_chunk<T, DK>(a.chunk);
     *chunk_used = c;
@@ -96,25 +96,25 @@ hipError_t run_dk(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_use
     if (!launch) return hipSuccess;
     switch (c) {
 #if KDA_CHUNK_MAX >= 64
-        case 64: return run_bv<T, TO, DK, 64, GZ>(a, s);
+        case 64: return run_bv<T, TO, DK, 64, GM>(a, s);
 #endif
 #if KDA_CHUNK_MAX >= 32
-        case 32: return run_bv<T, TO, DK, 32, GZ>(a, s);
+        case 32: return run_bv<T, TO, DK, 32, GM>(a, s);
 #endif
-        default: return run_bv<T, TO, DK, 16, GZ>(a, s);
+        default: return run_bv<T, TO, DK, 16, GM>(a, s);
     }
 }
 
-// GZ: the fused bounded gate (ChunkArgs::gz and friends) instead of g.
-template <class T, class TO, bool GZ>
+// GM: the gate mode (kGatePlain, kGateFused: ChunkArgs::gz and friends, kGateHead: g [T, H]).
+template <class T, class TO, int GM>
 hipError_t dispatch(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used) {
     *chunk_used = 0;
     if (a.dv != 16 && a.dv != 32 && a.dv != 64 && a.dv != 128) return hipErrorNotSupported;
     switch (a.dk) {
-        case 16: return run_dk<T, TO, 16, GZ>(a, s, launch, chunk_used);
-        case 32: return run_dk<T, TO, 32, GZ>(a, s, launch, chunk_used);
-        case 64: return run_dk<T, TO, 64, GZ>(a, s, launch, chunk_used);
-        case 128: return run_dk<T, TO, 128, GZ>(a, s, launch, chunk_used);
+        case 16: return run_dk<T, TO, 16, GM>(a, s, launch, chunk_used);
+        case 32: return run_dk<T, TO, 32, GM>(a, s, launch, chunk_used);
+        case 64: return run_dk<T, TO, 64, GM>(a, s, launch, chunk_used);
+        case 128: return run_dk<T, TO, 128, GM>(a, s, launch, chunk_used);
     }
     return hipErrorNotSupported;
 }

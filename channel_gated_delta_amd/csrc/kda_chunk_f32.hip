@@ -3,6 +3,6 @@
 
 namespace kda {
 hipError_t launch_chunk_f32(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used) {
-    return chunk_detail::dispatch<float, float, false>(a, s, launch, chunk_used);
+    return chunk_detail::dispatch<float, float, kGatePlain>(a, s, launch, chunk_used);
 }
 }  // namespace kda

@@ -1,0 +1,10 @@
+// Fp32 instantiations of the chunkwise prefill with one decay per
+// (token, head): the head-wise forget gate of GDN, g [T, H] broadcast to every
+// key channel.
+#include "kda_chunk_dispatch.cuh"
+
+namespace kda {
+hipError_t launch_chunk_f32_gdn(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used) {
+    return chunk_detail::dispatch<float, float, kGateHead>(a, s, launch, chunk_used);
+}
+}  // namespace kda

@@ -4,6 +4,6 @@
 
 namespace kda {
 hipError_t launch_chunk_f32_gz(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used) {
-    return chunk_detail::dispatch<float, float, true>(a, s, launch, chunk_used);
+    return chunk_detail::dispatch<float, float, kGateFused>(a, s, launch, chunk_used);
 }
 }  // namespace kda

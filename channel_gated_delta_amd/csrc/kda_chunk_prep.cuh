@@ -64,7 +64,7 @@ struct PrepCfg {
     static constexpr int kMinWg = kLds <= 53 * 1024 ? 3 : (kLds <= 80 * 1024 ? 2 : 1);
 };
 
-template <class T, int DK, int C, bool GZ>
+template <class T, int DK, int C, int GM>
 __global__ __launch_bounds__(256, (PrepCfg<T, DK, C>::kMinWg))
 void chunk_prep_kernel(const T *__restrict__ q, const T *__restrict__ k, GateSrc gs,
                        const float *__restrict__ beta,
@@ -104,7 +104,7 @@ void chunk_prep_kernel(const T *__restrict__ q, const T *__restrict__ k, GateSrc
     const bool fthread = part < NPART;
     // fused gate: this thread's constants for channels 2cp, 2cp+1
     float gc1 = 0.f, gc2a = 0.f, gc2b = 0.f, glb = 0.f;
-    if constexpr (GZ) {
+    if constexpr (GM == kGateFused) {
         gc1 = gate_c1(gs, h);
         gc2a = gate_c2(gs, gc1, h, DK, 2 * cp);
         gc2b = gate_c2(gs, gc1, h, DK, 2 * cp + 1);
@@ -144,10 +144,12 @@ void chunk_prep_kernel(const T *__restrict__ q, const T *__restrict__ k, GateSrc
                 const size_t off = (size_t)(cs + r) * rowQK + (size_t)h * DK + 2 * cp;
                 qr[j] = *reinterpret_cast<const T2 *>(q + off);
                 kr[j] = *reinterpret_cast<const T2 *>(k + off);
-                if constexpr (GZ) {
+                if constexpr (GM == kGateFused) {
                     const T2 zr = *reinterpret_cast<const T2 *>(static_cast<const T *>(gs.z) + off);
                     gr[j][0] = gate_log2(to_f32(zr[0]), gc1, gc2a, glb);
                     gr[j][1] = gate_log2(to_f32(zr[1]), gc1, gc2b, glb);
+                } else if constexpr (GM == kGateHead) {
+                    gr[j][0] = gr[j][1] = gs.g[(size_t)(cs + r) * H + h] * kLog2e;
                 } else {
                     const f32x2 gv = *reinterpret_cast<const f32x2 *>(gs.g + off);
                     gr[j][0] = gv[0] * kLog2e;
@@ -362,7 +364,7 @@ __device__ __forceinline__ float row_shr_zero(float v) {   // lane l%16 >= S: la
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + S, 0xf, 0xf, false));
 }
 
-template <int DK, bool GZ>
+template <int DK, int GM>
 __global__ __launch_bounds__(256, KDA_PREP16_MINB)
 void chunk_prep16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k, GateSrc gs,
                          const float *__restrict__ beta,
@@ -381,7 +383,7 @@ void chunk_prep16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const size_t rowQK = (size_t)H * DK;
     const int t = lane & 15, kb = lane >> 4;
     float gc1 = 0.f, glb = 0.f;   // fused gate: this head's constants
-    if constexpr (GZ) {
+    if constexpr (GM == kGateFused) {
         gc1 = gate_c1(gs, h);
         glb = gs.lb * kLog2e;
     }
@@ -416,7 +418,12 @@ void chunk_prep16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             const bf16x8 qr = *reinterpret_cast<const bf16x8 *>(q + off + 32 * j);
             const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(k + off + 32 * j);
             float x[8], qd[8], kd[8], kc[8];
-            if constexpr (GZ) {
+            if constexpr (GM == kGateHead) {
+                // one decay per (token, head): the same for the lane's 8 channels
+                const float xh = gs.g[(size_t)(cs + min(t, nt - 1)) * H + h] * kLog2e;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = xh;
+            } else if constexpr (GM == kGateFused) {
                 const bf16x8 zr = *reinterpret_cast<const bf16x8 *>(
                     static_cast<const bf16 *>(gs.z) + off + 32 * j);
                 const int c0 = 32 * j + 8 * kb;

@@ -244,7 +244,7 @@ __device__ __forceinline__ void state_chain_bf16(
     }
 }
 
-template <class T, class TO, int DK, int BV, int C, bool GZ>
+template <class T, class TO, int DK, int BV, int C, int GM>
 __global__ __launch_bounds__((StateCfg<T, DK, BV, C>::NT), 1)
 void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                         GateSrc gs, const float *__restrict__ tb,
@@ -286,7 +286,7 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
         const int pw = wave - 4;
         const int cpair = pw * CPW + (lane % CPW);            // channels 2cpair, 2cpair+1
         float gc1 = 0.f, gc2a = 0.f, gc2b = 0.f, glb = 0.f;   // fused gate constants
-        if constexpr (GZ) {
+        if constexpr (GM == kGateFused) {
             gc1 = gate_c1(gs, h);
             gc2a = gate_c2(gs, gc1, h, DK, 2 * cpair);
             gc2b = gate_c2(gs, gc1, h, DK, 2 * cpair + 1);
@@ -304,7 +304,9 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
         constexpr int NTB4 = NTB >= 4 ? NTB / 4 : 1;
         struct Regs {
             T2 q[RP], k[RP];
-            typename std::conditional<GZ, T2, f32x2>::type g[RP];   // g, or the gate's z
+            // g (two channels), the gate's z, or the per-head decay of the row
+            typename std::conditional<GM == kGateFused, T2,
+                typename std::conditional<GM == kGateHead, float, f32x2>::type>::type g[RP];
             f32x4 tb[NTB4], pm[NTB4];   // NTB == 1 uses element 0 of the first vector
             TV v;
         };
@@ -323,8 +325,11 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                                          (uint32_t)(2 * cpair);
                     R.q[j] = ld_off<T2>(qb, off * (uint32_t)sizeof(T));
                     R.k[j] = ld_off<T2>(kb, off * (uint32_t)sizeof(T));
-                    if constexpr (GZ)
+                    if constexpr (GM == kGateFused)
                         R.g[j] = ld_off<T2>(zb, off * (uint32_t)sizeof(T));
+                    else if constexpr (GM == kGateHead)
+                        R.g[j] = ld_off<float>(gs.g + (size_t)cs * H + h,
+                                               (uint32_t)min(rg * RP + j, last) * (uint32_t)H * 4u);
                     else
                         R.g[j] = ld_off<f32x2>(gb, off * 4u);
                 }
@@ -366,9 +371,13 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                 qv[j][1] = to_f32(cur.q[j][1]);
                 kv[j][0] = to_f32(cur.k[j][0]);
                 kv[j][1] = to_f32(cur.k[j][1]);
-                if constexpr (GZ) {
+                if constexpr (GM == kGateFused) {
                     a0 += in ? gate_log2(to_f32(cur.g[j][0]), gc1, gc2a, glb) : 0.f;
                     a1 += in ? gate_log2(to_f32(cur.g[j][1]), gc1, gc2b, glb) : 0.f;
+                } else if constexpr (GM == kGateHead) {
+                    const float xh = (in ? cur.g[j] : 0.f) * kLog2e;
+                    a0 += xh;
+                    a1 += xh;
                 } else {
                     a0 += (in ? cur.g[j][0] : 0.f) * kLog2e;
                     a1 += (in ? cur.g[j][1] : 0.f) * kLog2e;

@@ -79,7 +79,7 @@ __device__ __forceinline__ void conv_shift(const ConvTap<T> &c) {
     c.cache[2 * c.row] = c.x[3];
 }
 
-template <class T, class TO, int DK, int DV, bool CONV>
+template <class T, class TO, int DK, int DV, bool CONV, bool HG>   // HG: g is [B, H]
 __global__ __launch_bounds__(1024)
 void decode_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                    const float *__restrict__ g, const float *__restrict__ beta,
@@ -107,7 +107,7 @@ void decode_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     // channel DK-1 again and use nothing), so the loads need no branch.
     static_assert(NT >= DK, "one thread per key channel");
     const size_t kc_off = (size_t)bh * DK + min(tid, DK - 1);
-    const float g_in = g[kc_off];
+    const float g_in = HG ? g[bh] : g[kc_off];
     T q_in{}, k_in{};
     if constexpr (!CONV) {
         q_in = q[kc_off];
@@ -232,16 +232,16 @@ void decode_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     }
 }
 
-template <class T, int DK, int DV, bool CONV>
+template <class T, int DK, int DV, bool CONV, bool HG>
 hipError_t launch_conv_or_not(const DecodeArgs &a, hipStream_t s) {
     const int blocks = a.batch * a.heads;
     if (a.out_f32)
-        hipLaunchKernelGGL((decode_kernel<T, float, DK, DV, CONV>), dim3(blocks),
+        hipLaunchKernelGGL((decode_kernel<T, float, DK, DV, CONV, HG>), dim3(blocks),
                            dim3(DecodeCfg<T, DK, DV>::kThreads), 0, s,
                            (const T *)a.q, (const T *)a.k, (const T *)a.v, a.g, a.beta, a.state,
                            a.scale, (float *)a.o, a.conv);
     else
-        hipLaunchKernelGGL((decode_kernel<T, T, DK, DV, CONV>), dim3(blocks),
+        hipLaunchKernelGGL((decode_kernel<T, T, DK, DV, CONV, HG>), dim3(blocks),
                            dim3(DecodeCfg<T, DK, DV>::kThreads), 0, s,
                            (const T *)a.q, (const T *)a.k, (const T *)a.v, a.g, a.beta, a.state,
                            a.scale, (T *)a.o, a.conv);
@@ -251,8 +251,9 @@ hipError_t launch_conv_or_not(const DecodeArgs &a, hipStream_t s) {
 template <class T, int DK, int DV>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
     if (a.batch * a.heads == 0) return hipSuccess;
-    return a.with_conv ? launch_conv_or_not<T, DK, DV, true>(a, s)
-                       : launch_conv_or_not<T, DK, DV, false>(a, s);
+    if (a.head_gate) return launch_conv_or_not<T, DK, DV, false, true>(a, s);
+    return a.with_conv ? launch_conv_or_not<T, DK, DV, true, false>(a, s)
+                       : launch_conv_or_not<T, DK, DV, false, false>(a, s);
 }
 
 template <class T, int DK>

@@ -72,6 +72,7 @@ struct DecodeArgs {
     bool out_f32;   // o in fp32 (else in the input dtype)
     bool with_conv;
     DecodeConvIn conv;
+    bool head_gate;  // g is [B, H]: one decay per (sequence, head) (GDN's gate)
 };
 
 // Each launcher returns hipSuccess, hipErrorNotSupported for a shape it has no
@@ -86,6 +87,10 @@ hipError_t launch_chunk_f32(const ChunkArgs &a, hipStream_t s, bool launch, int 
 hipError_t launch_chunk_bf16_f32out_gz(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
 hipError_t launch_chunk_bf16_bf16out_gz(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
 hipError_t launch_chunk_f32_gz(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
+// The same with one decay per (token, head): ChunkArgs::g is [T, H] (GDN's gate).
+hipError_t launch_chunk_bf16_f32out_gdn(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
+hipError_t launch_chunk_bf16_bf16out_gdn(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
+hipError_t launch_chunk_f32_gdn(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_used);
 typedef hipError_t (*ChunkLauncher)(const ChunkArgs &, hipStream_t, bool, int *);
 hipError_t launch_decode_step(const DecodeArgs &a, bool bf16, hipStream_t s);
 // o_bf16: o is bf16 (needs bf16 gate / y); y_bf16: gate and y are bf16.

@@ -22,6 +22,8 @@ dtype; "N(0, s)" means standard deviation s):
   fp32 [H, D]
 * output-epilogue inputs (make_epilogue, seed + 2000): output-gate pre-activation
   N(0, 1) in the activation dtype [T, H, DV], norm weight 1 + N(0, 0.1) fp32 [DV]
+* per-head decay for the GDN variant (make_head_gate, seed + 4000): lb * sigmoid(N(0,
+  gate_std)) fp32 [T, H] (decode: [B, H] per step, make_decode_step's generator)
 * decode with the conv (make_decode_conv, seed + 3000): conv weights N(0, 0.5) and
   initial conv caches N(0, 1) (raw inputs) in the activation dtype; per step
   (make_decode_conv_step) raw projections N(0, 1) and g, beta as above
@@ -149,6 +151,13 @@ def make_prefill(spec: PrefillSpec, device="cpu") -> Dict[str, torch.Tensor]:
     out["cu_seqlens"] = torch.tensor(cu_seqlens_of(spec.lengths), dtype=torch.int32,
                                      device=device)
     return out
+
+
+def make_head_gate(spec: PrefillSpec, device="cpu") -> torch.Tensor:
+    """One log-decay per (token, head) for the GDN variant: g [T, H] fp32 (own seed)."""
+    gen = _gen(device, spec.seed + 4000)
+    z = _normal((spec.total_tokens, spec.heads), gen, device, spec.gate_std)
+    return (spec.gate_lb * torch.sigmoid(z)).float()
 
 
 def make_epilogue(spec: PrefillSpec, device="cpu") -> Dict[str, torch.Tensor]:

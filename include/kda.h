@@ -219,6 +219,32 @@ KDA_API kda_status_t kda_decode_step(const void *q, const void *k, const void *v
                              kda_dtype_t out_dtype, void *stream);
 
 /*
+ * kda_gdn_chunk_fwd, kda_gdn_decode_step -- the same computations with one
+ * decay per (token, head) instead of one per key channel: the head-wise forget
+ * gate of Gated DeltaNet (GDN), which the pages set against KDA's channel-wise
+ * one ([Replication-1]: GDN scales a head's whole state by one scalar).  The
+ * recurrence is KDA's with g[t, h, c] = g[t, h] for every key channel c.
+ *
+ *   g   [total_tokens, num_heads] fp32 (chunk) / [batch, num_heads] fp32 (decode),
+ *       gate_lower_bound <= g <= 0 for the chunk call.
+ * Every other argument, the workspace, the supported shapes and the errors are
+ * those of kda_chunk_fwd and kda_decode_step.
+ */
+KDA_API kda_status_t kda_gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                                       const float *beta, const int32_t *cu_seqlens,
+                                       int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                       int32_t dk, int32_t dv, int32_t chunk_size, float scale,
+                                       float gate_lower_bound, const float *initial_state,
+                                       float *final_state, void *o, void *workspace,
+                                       size_t workspace_bytes, kda_dtype_t dtype,
+                                       kda_dtype_t out_dtype, void *stream);
+KDA_API kda_status_t kda_gdn_decode_step(const void *q, const void *k, const void *v,
+                                         const float *g, const float *beta, float *state,
+                                         int32_t batch, int32_t num_heads, int32_t dk, int32_t dv,
+                                         float scale, void *o, kda_dtype_t dtype,
+                                         kda_dtype_t out_dtype, void *stream);
+
+/*
  * kda_decode_step_conv -- one generation step from this token's raw q/k/v
  * projections: the prologue of kda_short_conv (width-4 causal conv over the
  * conv cache, SiLU, q and k scaled to unit length; [Walkthrough] 第二站) and

@@ -34,8 +34,9 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"kda_short_conv", "kda_chunk_fwd", "kda_chunk_fwd_gated",
                           "kda_chunk_fwd_workspace_size", "kda_decode_step",
-                          "kda_output_norm_gate", "kda_decode_step_conv", "kda_status_string",
-                          "kda_last_error", "kda_version"}
+                          "kda_output_norm_gate", "kda_decode_step_conv", "kda_gdn_chunk_fwd",
+                          "kda_gdn_decode_step", "kda_status_string", "kda_last_error",
+                          "kda_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -111,6 +112,29 @@ def test_workspace_size(lib):
 def test_chunk_fwd_rejects(lib, kw, status):
     assert chunk(lib, **kw) == status
     assert lib.kda_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=NULL), kda.KDA_ERR_INVALID_ARG),
+    (dict(o=P), kda.KDA_ERR_INVALID_ARG),
+    (dict(lb=-9.5), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dk=48), kda.KDA_ERR_UNSUPPORTED),
+    (dict(wsb=2 * 64 * 2 * 16 * 4 - 1), kda.KDA_ERR_INVALID_ARG),
+])
+def test_gdn_calls_reject(lib, kw, status):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, cu=NULL, N=1, T=64, H=2, dk=128, dv=128, chunk=64,
+             scale=0.1, lb=-5.0, h0=NULL, hT=NULL, o=ctypes.c_void_p(8192),
+             ws=ctypes.c_void_p(1 << 20), wsb=1 << 30, dtype=BF16, odt=F32)
+    a.update(kw)
+    assert lib.kda_gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"],
+                                 a["T"], a["H"], a["dk"], a["dv"], a["chunk"], a["scale"],
+                                 a["lb"], a["h0"], a["hT"], a["o"], a["ws"], a["wsb"],
+                                 a["dtype"], a["odt"], NULL) == status
+    assert b"kda_gdn_chunk_fwd" in lib.kda_last_error()
+    st = lib.kda_gdn_decode_step(P, P, P, a["g"], P, ctypes.c_void_p(12288), 4, 2, a["dk"], 128,
+                                 0.1, a["o"], BF16, F32, NULL)
+    if "g" in kw or "o" in kw or "dk" in kw:
+        assert st == status and b"kda_gdn_decode_step" in lib.kda_last_error()
 
 
 def chunk_gated(lib, **kw):

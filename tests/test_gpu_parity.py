@@ -196,6 +196,69 @@ def test_gated_matches_plain_gate():
     assert_parity("state fused vs plain", to64(got["hT"]), to64(plain["hT"]), 1e-3)
 
 
+# ------------------------------------------------------------------ GDN: one decay per head
+
+def check_gdn(spec):
+    inp = workloads.make_prefill(spec, DEV)
+    gh = workloads.make_head_gate(spec, DEV)
+    T, H, DK = spec.total_tokens, spec.heads, spec.dk
+    o, hT = kda.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], gh, inp["beta"],
+                              cu_seqlens=inp["cu_seqlens"], scale=spec.read_scale,
+                              gate_lower_bound=spec.gate_lb, chunk_size=spec.chunk,
+                              initial_state=inp["h0"])
+    torch.cuda.synchronize()
+    # the oracle's recurrence with the head's decay on every key channel
+    g = np.repeat(to64(gh)[:, :, None], DK, axis=2)
+    h0 = None if inp["h0"] is None else to64(inp["h0"])
+    ro, rh = oracle.recurrent(to64(inp["q"]), to64(inp["k"]), to64(inp["v"]), g,
+                              to64(inp["beta"]), inp["cu_seqlens"].cpu().numpy(), spec.read_scale,
+                              h0)
+    tol = tol_for(spec.dtype)
+    assert_parity("o (GDN)", to64(o), ro, tol)
+    assert_parity("final state (GDN)", to64(hT), rh, tol)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (16, 16), (32, 64), (128, 16)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_gdn_chunk(dk, dv, dtype):
+    note("GDN chunk dk=%d dv=%d %s" % (dk, dv, dtype))
+    check_gdn(spec_of(RAGGED, H=2, dk=dk, dv=dv, dtype=dtype, h0=0.05, seed=41 + dk))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_gdn_strong_decay(dtype):
+    check_gdn(spec_of([300, 41], H=3, dtype=dtype, lb=-8.0, gate_std=2.0, h0=0.05, seed=43))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_gdn_decode(dtype):
+    """GDN decode steps against the oracle's recurrence with the decay broadcast."""
+    B, H, dk, dv, steps = 3, 2, 128, 64, 6
+    spec = workloads.DecodeSpec("t", batch=B, heads=H, dk=dk, dv=dv, steps=steps, dtype=dtype,
+                                seed=44)
+    state = workloads.make_decode_state(spec, DEV)
+    s0 = to64(state)
+    ins, outs = [], []
+    for t in range(steps):
+        d = workloads.make_decode_step(spec, t, DEV)
+        d["g"] = d["g"][:, :, 0].contiguous()       # one decay per (sequence, head)
+        outs.append(kda.gdn_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state))
+        ins.append(d)
+    torch.cuda.synchronize()
+
+    def packed(key):
+        x = torch.stack([i[key] for i in ins], dim=1)
+        return to64(x.reshape(B * steps, *x.shape[2:]))
+
+    g = np.repeat(packed("g")[:, :, None], dk, axis=2)
+    cu = np.arange(B + 1) * steps
+    o, hT = oracle.recurrent(packed("q"), packed("k"), packed("v"), g, packed("beta"), cu,
+                             dk ** -0.5, s0)
+    tol = tol_for(dtype)
+    assert_parity("GDN decode o", to64(torch.stack(outs, dim=1).reshape(B * steps, H, dv)), o, tol)
+    assert_parity("GDN decode state", to64(state), hT, tol)
+
+
 # ------------------------------------------------------------------ decode with the conv
 
 def decode_conv_case(B, H, dk, dv, steps, dtype, seed):

@@ -82,6 +82,28 @@ def test_prefill_workload_output_epilogue():
 
 
 @pytest.mark.timeout(600)
+def test_prefill_workload_gdn():
+    """The prefill workload (conv prologue on the GPU) with one decay per (token, head)."""
+    spec = workloads.standard_specs()["prefill"]
+    inp = workloads.make_prefill(spec, DEV)
+    gh = workloads.make_head_gate(spec, DEV)
+    H, DK, DV = spec.heads, spec.dk, spec.dv
+    q, _ = kda.short_conv(inp["q_raw"], inp["w_q"], num_heads=H, head_dim=DK, l2_normalize=True)
+    k, _ = kda.short_conv(inp["k_raw"], inp["w_k"], num_heads=H, head_dim=DK, l2_normalize=True)
+    v, _ = kda.short_conv(inp["v_raw"], inp["w_v"], num_heads=H, head_dim=DV)
+    o, hT = kda.gdn_chunk_fwd(q, k, v, gh, inp["beta"], scale=spec.read_scale,
+                              gate_lower_bound=spec.gate_lb, chunk_size=spec.chunk)
+    torch.cuda.synchronize()
+    heads = [1, 47, 94]
+    cu = inp["cu_seqlens"].cpu().numpy()
+    g = np.repeat(to64(gh[:, heads])[:, :, None], DK, axis=2)
+    ro, rh = oracle.recurrent(to64(q[:, heads]), to64(k[:, heads]), to64(v[:, heads]), g,
+                              to64(inp["beta"][:, heads]), cu, spec.read_scale)
+    assert_parity("o (GDN, sampled heads)", to64(o[:, heads]), ro, 2e-2)
+    assert_parity("final state (GDN, sampled heads)", to64(hT[:, heads]), rh, 2e-2)
+
+
+@pytest.mark.timeout(600)
 def test_decode_conv_workload():
     """64 sequences x 96 heads, 8 fused steps (conv + SiLU + L2 + the recurrent step) from
     raw projections and conv caches; every (sequence, head) against the oracle."""
