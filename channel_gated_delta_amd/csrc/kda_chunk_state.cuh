@@ -132,16 +132,14 @@ __device__ __forceinline__ void state_chain_bf16(
     }
 
     // E = Kd S, O = Qd S: k-block j's products while block j+1 loads.  The three
-    // split terms go to separate accumulators (summed at the end), so 6 NTC
-    // independent accumulation chains interleave.
-    f32x4 Et3[3][NTC], Ot3[3][NTC];
+    // split terms accumulate in place (an MFMA that depends on the one before it
+    // issues at the same rate), E and O products alternating.
+    f32x4 Et[NTC];
 #pragma unroll
-    for (int t = 0; t < 3; ++t)
-#pragma unroll
-        for (int R = 0; R < NTC; ++R) {
-            Et3[t][R] = f32x4{0.f, 0.f, 0.f, 0.f};
-            Ot3[t][R] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+    for (int R = 0; R < NTC; ++R) {
+        Et[R] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Ot[R] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     // The state is split into (hi, lo) B operands here, block by block: block j+1's
     // split runs beside block j's products instead of after the previous update.
     sb[0] = breg8(Sacc[0], Sacc[1]);
@@ -157,27 +155,17 @@ __device__ __forceinline__ void state_chain_bf16(
         }
         __builtin_amdgcn_sched_barrier(0);
         if (j + 1 < NKB) sb[j + 1] = breg8(Sacc[2 * j + 2], Sacc[2 * j + 3]);
-        // term-major order: the 2*NTC accumulators interleave, so no product waits
-        // for the one before it
 #pragma unroll
         for (int R = 0; R < NTC; ++R) {
-            Et3[0][R] = mma(fk[cur][R].h, sb[j].h, Et3[0][R]);
-            Ot3[0][R] = mma(fq[cur][R].h, sb[j].h, Ot3[0][R]);
-            Et3[1][R] = mma(fk[cur][R].h, sb[j].l, Et3[1][R]);
-            Ot3[1][R] = mma(fq[cur][R].h, sb[j].l, Ot3[1][R]);
-            Et3[2][R] = mma(fk[cur][R].l, sb[j].h, Et3[2][R]);
-            Ot3[2][R] = mma(fq[cur][R].l, sb[j].h, Ot3[2][R]);
+            Et[R] = mma(fk[cur][R].h, sb[j].h, Et[R]);
+            Ot[R] = mma(fq[cur][R].h, sb[j].h, Ot[R]);
+            Et[R] = mma(fk[cur][R].h, sb[j].l, Et[R]);
+            Ot[R] = mma(fq[cur][R].h, sb[j].l, Ot[R]);
+            Et[R] = mma(fk[cur][R].l, sb[j].h, Et[R]);
+            Ot[R] = mma(fq[cur][R].l, sb[j].h, Ot[R]);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
-    f32x4 Et[NTC];
-#pragma unroll
-    for (int R = 0; R < NTC; ++R)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            Et[R][r] = Et3[0][R][r] + (Et3[1][R][r] + Et3[2][R][r]);
-            Ot[R][r] = Ot3[0][R][r] + (Ot3[1][R][r] + Ot3[2][R][r]);
-        }
     // first half of the state-update fragments load during the U and P U products
     constexpr int NK1 = NTK / 2;
     AF8 fr8[NTK];
@@ -519,11 +507,13 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
         // (hi, lo) B operands of the state, built block by block inside each chain
         constexpr int NKB = DK / 32 > 0 ? DK / 32 : 1;
         BReg8 sbs[NKB];
-        for (int s = 0; s < nsteps; ++s) {
+        // Step s consumes chunk s-1 from stage (s-1) & 1; the loop runs steps in pairs so
+        // that the stage (and every LDS address below) is a constant of the code.
+        auto cstep = [&](int s, const int stage) {
             if (s >= 1 && s <= nchunks && owner) {
                 const int64_t c0 = bos + (int64_t)(s - 1) * C;
                 const int nt = (int)min((int64_t)C, eos - c0);
-                const char *st = smem + ((s - 1) & 1) * Cfg::kStage;
+                const char *st = smem + stage * Cfg::kStage;
                 const T *sQdh = reinterpret_cast<const T *>(st + Cfg::oQd);
                 const T *sQdl = sQdh + (SPLIT ? CKE : 0);
                 const T *sKdh = reinterpret_cast<const T *>(st + Cfg::oKd);
@@ -543,16 +533,21 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                                                            sKrTh, sKrTl, sTbh, sTbl, sPh, sPl, sV,
                                                            sEGn, wave * 16, lane);
                     TO *ob = o + (size_t)c0 * rowV + (size_t)h * DV;
+                    auto store = [&](bool all) {
 #pragma unroll
-                    for (int R = 0; R < NTC; ++R)
+                        for (int R = 0; R < NTC; ++R)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int row = R * 16 + acc_row(lane, r);
-                            if (row < nt)
-                                st_off<TO>(ob, ((uint32_t)row * (uint32_t)rowV + (uint32_t)vc) *
-                                                   (uint32_t)sizeof(TO),
-                                           from_f32<TO>(Ot[R][r]));
-                        }
+                            for (int r = 0; r < 4; ++r) {
+                                const int row = R * 16 + acc_row(lane, r);
+                                if (all || row < nt)
+                                    st_off<TO>(ob, ((uint32_t)row * (uint32_t)rowV + (uint32_t)vc) *
+                                                       (uint32_t)sizeof(TO),
+                                               from_f32<TO>(Ot[R][r]));
+                            }
+                    };
+                    // whole chunks (all but a sequence's last) store without a row test
+                    if (nt == C) store(true);
+                    else store(false);
                 } else {
                 RegB<T, NTK> Sb;
                 Sb.prepare(Sacc);
@@ -598,6 +593,11 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                 }
                 }
             }
+        };
+        for (int s = 0; s < nsteps; s += 2) {   // nsteps is even
+            cstep(s, 1);
+            lds_barrier();
+            cstep(s + 1, 0);
             lds_barrier();
         }
         if (hT && owner) {
