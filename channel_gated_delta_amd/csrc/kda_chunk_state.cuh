@@ -11,7 +11,7 @@
 //    wave from registers -- an accumulator tile doubles as the B operand of the
 //    next product when the A fragment is read with the matching k order.
 //  * producer waves 4..7 build the next chunk's operands in the other half of a
-//    double-buffered LDS stage: scale q e^{G}, k e^{G} and (k e^{G_n - G})^T
+//    double-buffered LDS stage: q e^{G}, k e^{G} and (k e^{G_n - G})^T
 //    (all factors <= 1, exponentiated directly), the split Tb and P rows, V and
 //    e^{G_n}.  A producer lane owns two key channels of a group of rows; the
 //    in-chunk prefix of the log-decay over row groups is a few lane shuffles,
@@ -63,7 +63,7 @@ struct StateCfg {
     static constexpr size_t szCK = al((size_t)C * LDK * sizeof(T));      // [C][DK]
     static constexpr size_t szKC = al((size_t)DK * LDC * sizeof(T));     // [DK][C]
     static constexpr size_t szCC = al((size_t)C * LDC * sizeof(T));      // [C][C]
-    static constexpr size_t oQd = 0;                                // scale q e^G (hi, lo)
+    static constexpr size_t oQd = 0;                                // q e^G (hi, lo)
     static constexpr size_t oKd = oQd + NSPLIT * szCK;              // k e^G (hi, lo)
     static constexpr size_t oKrT = oKd + NSPLIT * szCK;             // (k e^{Gn-G})^T (hi, lo)
     static constexpr size_t oTb = oKrT + NSPLIT * szKC;             // Tb (hi, lo)
@@ -109,7 +109,7 @@ __device__ __forceinline__ void state_chain_bf16(
     f32x4 (&Sacc)[DK / 16], BReg8 (&sb)[DK / 32], f32x4 (&Ot)[C / 16], const bf16 *sQdh, const bf16 *sQdl,
     const bf16 *sKdh, const bf16 *sKdl, const bf16 *sKrTh, const bf16 *sKrTl, const bf16 *sTbh,
     const bf16 *sTbl, const bf16 *sPh, const bf16 *sPl, const float *sV, const float *sEGn,
-    int wcol, int lane) {
+    float scale, int wcol, int lane) {
     constexpr int NTK = DK / 16, NKB = DK / 32, NTC = C / 16;
     static_assert(DK % 32 == 0 && (C == 16 || C == 32), "shape");
     // small operands first: Tb / P fragments and V
@@ -176,11 +176,14 @@ __device__ __forceinline__ void state_chain_bf16(
         else fr4[rt] = lda4(sKrTh, sKrTl, LDC, rt * 16, 0, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // E = V - Kd S;  U = Tb E
+    // E = V - Kd S;  U = Tb E;  O = scale Qd S (the stage holds q e^G unscaled)
 #pragma unroll
     for (int R = 0; R < NTC; ++R)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Et[R][r] = vin[R][r] - Et[R][r];
+        for (int r = 0; r < 4; ++r) {
+            Et[R][r] = vin[R][r] - Et[R][r];
+            Ot[R][r] *= scale;
+        }
     f32x4 Ut[NTC];
     BReg8 ub8;
     BReg4 ub4;
@@ -349,7 +352,7 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
             // row.  Only g (so the decay stops there) and the Tb, P rows are zeroed:
             // zero rows of Tb make U zero there, which removes every other
             // contribution of those rows (V, k e^G, k e^{Gn-G}); their rows of
-            // scale q e^G only produce outputs that are never stored.
+            // q e^G only produce outputs that are never stored.
             float qv[RP][2], kv[RP][2], gam[RP][2];
             float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -453,7 +456,7 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                     krt[0][j] = kv[j][0] * exp2_nonpos(tot0 - g0);
                     krt[1][j] = kv[j][1] * exp2_nonpos(tot1 - g1);
                     const int i = (rg * RP + j) * LDK + 2 * cpair;
-                    put2(sQdh, sQdl, i, qv[j][0] * e0 * scale, qv[j][1] * e1 * scale);
+                    put2(sQdh, sQdl, i, qv[j][0] * e0, qv[j][1] * e1);
                     put2(sKdh, sKdl, i, kv[j][0] * e0, kv[j][1] * e1);
                 }
 #pragma unroll
@@ -531,7 +534,7 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                     f32x4 Ot[NTC];
                     state_chain_bf16<DK, C, LDK, LDC, LDV>(Sacc, sbs, Ot, sQdh, sQdl, sKdh, sKdl,
                                                            sKrTh, sKrTl, sTbh, sTbl, sPh, sPl, sV,
-                                                           sEGn, wave * 16, lane);
+                                                           sEGn, scale, wave * 16, lane);
                     TO *ob = o + (size_t)c0 * rowV + (size_t)h * DV;
                     auto store = [&](bool all) {
 #pragma unroll
@@ -552,11 +555,13 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                 RegB<T, NTK> Sb;
                 Sb.prepare(Sacc);
                 f32x4 Et[NTC], Ot[NTC], Ut[NTC];
-                // E = V - Kd S and O = Qd S
+                // E = V - Kd S and O = scale Qd S
 #pragma unroll
                 for (int R = 0; R < NTC; ++R) {
                     Et[R] = Sb.mul(f32x4{0.f, 0.f, 0.f, 0.f}, sKdh, sKdl, LDK, R * 16, NTK, lane);
                     Ot[R] = Sb.mul(f32x4{0.f, 0.f, 0.f, 0.f}, sQdh, sQdl, LDK, R * 16, NTK, lane);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Ot[R][r] *= scale;
                 }
 #pragma unroll
                 for (int R = 0; R < NTC; ++R)
