@@ -4,18 +4,28 @@
 
 A step is one pass of the prefill path over one batch of synthetic input resident
 in HBM: the conv4 + SiLU (+ q/k L2) prologue on q, k, v followed by the
-chunkwise KDA kernel (B=1, T=4096, H=96, dk=dv=128, chunk 64, bf16; final state
-written).  ``value`` is prefill tokens/s.  The same JSON line carries:
+chunkwise KDA call (B=1, T=4096, H=96, dk=dv=128, bf16; chunk 64 requested, the
+kernels walk 16-token chunks; final state written).  ``value`` is prefill
+tokens/s.  The same JSON line carries:
 
-* ``roofline``: the chunk kernel's algorithmic HBM bytes per launch divided by
-  its average launch duration, timed with HIP events on the stream it runs on,
-  against the 8 TB/s HBM peak; ``traffic`` is the measured HBM traffic per launch
-  from the committed rocprofv3 counter summary when it was taken on the current
-  kernel source, else null;
+* ``roofline``: the chunk call's algorithmic HBM bytes per launch (q, k, v bf16,
+  g fp32, beta, o counted as bf16: 1540 B per token and head, plus the states)
+  divided by its average launch duration, timed with HIP events on the stream it
+  runs on, against the 8 TB/s HBM peak.  The call writes o in fp32 (1796 B per
+  token and head); ``frac_fp32_o`` is the fraction on those bytes.  ``traffic``
+  is the measured HBM traffic per launch from the committed rocprofv3 counter
+  summary when it was taken on the current kernel source, else null;
+* ``mfma``: the call's useful bf16 MFMA work (the chunk algorithm's product
+  flops, split terms not counted) per second against the 2.5 PFLOP/s dense peak;
+* ``hbm_copy``: a plain device-to-device copy of 1 GiB timed the same way (the
+  bandwidth this GPU attains on a streaming copy, beside the 8 TB/s spec);
+* ``varlen``, ``long``: the same step on the packed variable-length workload
+  (8 sequences, 32768 tokens, random h0) and the long-context workload
+  (131072 tokens, gates down to -8), with their chunk calls' rooflines;
 * ``decode``: 256 in-place decode steps of 64 sequences x 96 heads (steps/s) and
   the decode kernel's roofline;
-* ``fused_gate``: the same prefill step with the bounded gate formed inside the
-  chunk kernels from bf16 pre-activations (kda_chunk_fwd_gated) instead of a
+* ``fused_gate``: the prefill step with the bounded gate formed inside the chunk
+  kernels from bf16 pre-activations (kda_chunk_fwd_gated) instead of a
   precomputed fp32 g, and that call's roofline;
 * ``output_epilogue``: the per-head RMSNorm and sigmoid output gate applied to the
   step's fp32 read-out (bf16 gate in, bf16 y out), timed alone, and its roofline;
@@ -82,26 +92,37 @@ def measured_traffic(kind: str, workload: str):
     return float(t.group(1))
 
 
-def prefill_step_bytes(T: int, H: int, dk: int, dv: int, N: int, h0: bool) -> float:
-    """Algorithmic HBM bytes of one chunk-kernel launch: every tensor once.
+def prefill_step_bytes(T: int, H: int, dk: int, dv: int, N: int, h0: bool,
+                       o_bytes: int = 2) -> float:
+    """Algorithmic HBM bytes of one chunk call: every tensor once.
 
     per token per head: q, k (bf16) 2*2*dk + v (bf16) 2*dv + g (fp32) 4*dk + beta 4
-    + o (fp32) 4*dv; plus the final state (and the initial state when given).
+    + o (o_bytes per element: 2 counts it as bf16, 1540 B in all for d = 128; the
+    call's fp32 o is 4); plus the final state (and the initial state when given).
     """
-    per_tok_head = 2 * dk + 2 * dk + 2 * dv + 4 * dk + 4 + 4 * dv
+    per_tok_head = 2 * dk + 2 * dk + 2 * dv + 4 * dk + 4 + o_bytes * dv
     states = N * H * dk * dv * 4 * (2 if h0 else 1)
     return float(T * H * per_tok_head + states)
 
 
-def gdn_step_bytes(T: int, H: int, dk: int, dv: int, N: int, h0: bool) -> float:
+def prefill_useful_flops(T: int, H: int, dk: int, dv: int, C: int = 64) -> float:
+    """The chunk algorithm's useful product flops per call, per token and head
+    2 * [3 dk dv + (C / 2) (3 dk + 2 dv)] (the in-chunk triangles counted as half,
+    the O(C^2) solve left out), at the 64-token chunk the workload names."""
+    return float(T * H * 2 * (3 * dk * dv + (C // 2) * (3 * dk + 2 * dv)))
+
+
+def gdn_step_bytes(T: int, H: int, dk: int, dv: int, N: int, h0: bool,
+                   o_bytes: int = 2) -> float:
     """As prefill_step_bytes with one fp32 decay per (token, head) in place of g."""
-    return prefill_step_bytes(T, H, dk, dv, N, h0) - float(T * H * (4 * dk - 4))
+    return prefill_step_bytes(T, H, dk, dv, N, h0, o_bytes) - float(T * H * (4 * dk - 4))
 
 
-def gated_step_bytes(T: int, H: int, dk: int, dv: int, N: int, h0: bool) -> float:
+def gated_step_bytes(T: int, H: int, dk: int, dv: int, N: int, h0: bool,
+                     o_bytes: int = 2) -> float:
     """As prefill_step_bytes with the gate's bf16 pre-activation z (2*dk per token and
     head) in place of the fp32 g; A_log and dt_bias are negligible."""
-    return prefill_step_bytes(T, H, dk, dv, N, h0) - float(T * H * 2 * dk)
+    return prefill_step_bytes(T, H, dk, dv, N, h0, o_bytes) - float(T * H * 2 * dk)
 
 
 def decode_conv_step_bytes(B: int, H: int, dk: int, dv: int) -> float:
@@ -172,9 +193,10 @@ def decode_step_bytes(B: int, H: int, dk: int, dv: int) -> float:
     return float(B * H * (2 * dk * dv * 4 + 2 * dk * 2 + dv * 2 + 4 * dk + 4 + 4 * dv))
 
 
-def run_prefill(args, torch, kda, workloads, gated=False, gdn=False):
+def run_prefill(args, torch, kda, workloads, gated=False, gdn=False, workload=None, steps=None):
     specs = workloads.standard_specs()
-    spec = specs[args.workload]
+    spec = specs[workload or args.workload]
+    nsteps = steps or args.steps
     dev = "cuda:0"
     inp = workloads.make_prefill(spec, dev)
     gate = workloads.make_gate(spec, dev) if gated else None
@@ -221,19 +243,20 @@ def run_prefill(args, torch, kda, workloads, gated=False, gdn=False):
         step()
     torch.cuda.synchronize()
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+              for _ in range(nsteps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for i in range(args.steps):
+    for i in range(nsteps):
         step(events[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    chunk_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
-    ms_step = total_ms / args.steps
-    return dict(spec=spec, T=T, N=N, ms_step=ms_step, chunk_ms=chunk_ms, inp=inp, o=ob)
+    chunk_ms = sum(a.elapsed_time(b) for a, b in events) / nsteps
+    ms_step = total_ms / nsteps
+    return dict(spec=spec, T=T, N=N, ms_step=ms_step, chunk_ms=chunk_ms, inp=inp, o=ob,
+                steps=nsteps)
 
 
 def run_decode(torch, kda, workloads, steps=256, warmup=16):
@@ -315,6 +338,66 @@ def copy_calibration(torch, nbytes=1 << 30, reps=3):
     print(json.dumps({"copy_calibration_bytes": nbytes, "dispatches": reps}))
 
 
+def timed_copy(torch, nbytes=1 << 30, reps=20):
+    """GB/s of a plain device-to-device copy (1 GiB read + 1 GiB written per call),
+    timed with HIP events over ``reps`` back-to-back calls after two warm-ups."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return {"gbs": round(2 * nbytes / (ms / 1e3) / 1e9, 1), "bytes_per_call": 2 * nbytes,
+            "ms_per_call": round(ms, 4), "peak_spec_gbs": HBM_PEAK_GBS,
+            "what": "torch copy_ of 1 GiB fp32 (read + write), 20 calls"}
+
+
+def chunk_roofline(spec, res, kernel, bytes_fn, traffic_kind):
+    """Roofline of a chunk call: algorithmic bytes (o counted as bf16) over the call's
+    HIP-event time; the same with the fp32 o the call writes; measured traffic."""
+    H, DK, DV, T, N = spec.heads, spec.dk, spec.dv, res["T"], res["N"]
+    h0 = spec.h0_std is not None
+    alg = bytes_fn(T, H, DK, DV, N, h0, 2)
+    alg32 = bytes_fn(T, H, DK, DV, N, h0, 4)
+    sec = res["chunk_ms"] / 1e3
+    ach = alg / sec / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(traffic_kind, spec_key(spec)),
+            "kernel": kernel, "algorithmic_bytes_per_launch": alg,
+            "bytes_accounting": "q,k,v bf16 + g fp32 + beta + o as bf16 per token-head, + states",
+            "frac_fp32_o": round(alg32 / sec / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_fp32_o": alg32,
+            "avg_launch_ms": round(res["chunk_ms"], 4)}
+
+
+def spec_key(spec) -> str:
+    return spec.name.split()[0]
+
+
+def sub_line(args, torch, kda, workloads, name, steps):
+    """The prefill step on another workload: tokens/s and the chunk call's roofline."""
+    res = run_prefill(args, torch, kda, workloads, workload=name, steps=steps)
+    spec = res["spec"]
+    out = {"workload": spec.name, "value": round(res["T"] / (res["ms_step"] / 1e3), 1),
+           "unit": "tokens/s", "tokens": res["T"], "sequences": res["N"],
+           "ms_per_step": round(res["ms_step"], 4), "steps": res["steps"],
+           "chunk_tokens_per_s": round(res["T"] / (res["chunk_ms"] / 1e3), 1),
+           "roofline": chunk_roofline(spec, res, "kda_chunk_fwd (chunk_prep16_kernel + "
+                                      "chunk_state_kernel)", prefill_step_bytes, "chunk")}
+    del res
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -325,6 +408,9 @@ def main():
     ap.add_argument("--no-gate", action="store_true")
     ap.add_argument("--no-epilogue", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="skip the varlen and long-context sub-lines")
+    ap.add_argument("--no-copy", action="store_true", help="skip the timed 1 GiB copy")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (torch elementwise kernel), the "
                          "reference for scaling HBM byte counters")
@@ -352,14 +438,10 @@ def main():
     spec = res["spec"]
     H, DK, DV, T, N = spec.heads, spec.dk, spec.dv, res["T"], res["N"]
     tok_s = T / (res["ms_step"] / 1e3)
-    alg_bytes = prefill_step_bytes(T, H, DK, DV, N, spec.h0_std is not None)
-    achieved = alg_bytes / (res["chunk_ms"] / 1e3) / 1e9
-    traffic = measured_traffic("chunk", args.workload)
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "kda_chunk_fwd (chunk_prep16_kernel + chunk_state_kernel)",
-            "algorithmic_bytes_per_launch": alg_bytes,
-            "avg_launch_ms": round(res["chunk_ms"], 4)}
+    roof = chunk_roofline(spec, res, "kda_chunk_fwd (chunk_prep16_kernel + chunk_state_kernel)",
+                          prefill_step_bytes, "chunk")
+    useful = prefill_useful_flops(T, H, DK, DV, spec.chunk)
+    ut = useful / (res["chunk_ms"] / 1e3) / 1e12
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_step"], 4),
@@ -367,10 +449,24 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; no weights or datasets)",
         "config": {"workload": spec.name, "batch": N, "seq_len": T, "heads": H, "dk": DK,
-                   "dv": DV, "chunk": spec.chunk, "path": "3x short_conv (conv4+SiLU, q/k L2) + "
-                   "chunk_fwd"},
+                   "dv": DV, "chunk_requested": spec.chunk, "chunk_internal": 16,
+                   "path": "3x short_conv (conv4+SiLU, q/k L2) + chunk_fwd (fp32 o)"},
         "roofline": roof,
+        "mfma": {"useful_gflop_per_launch": round(useful / 1e9, 2),
+                 "useful_tflops": round(ut, 1), "peak_tflops": 2500.0,
+                 "frac_of_bf16_peak": round(ut / 2500.0, 4),
+                 "what": "chunk algorithm's product flops (64-token chunk, triangles halved, "
+                         "split-bf16 terms not counted) / the call's event time"},
     }
+    if not args.no_copy:
+        out["hbm_copy"] = timed_copy(torch)
+    keep_o = res["o"] if not args.no_epilogue else None
+    keep_res = {"spec": spec, "inp": res["inp"], "T": T} if not args.no_cpu else None
+    del res
+    torch.cuda.empty_cache()
+    if not args.no_sub and args.workload == "prefill":
+        out["varlen"] = sub_line(args, torch, kda, workloads, "varlen", args.steps)
+        out["long"] = sub_line(args, torch, kda, workloads, "long", min(args.steps, 10))
     if not args.no_decode:
         d = run_decode(torch, kda, workloads)
         ms_dec = d["ms"] / d["steps"]
@@ -398,36 +494,24 @@ def main():
                                            "algorithmic_bytes_per_launch": dbytes}}
     if not args.no_gate:
         gres = run_prefill(args, torch, kda, workloads, gated=True)
-        gbytes = gated_step_bytes(T, H, DK, DV, N, spec.h0_std is not None)
-        gach = gbytes / (gres["chunk_ms"] / 1e3) / 1e9
         out["fused_gate"] = {
             "value": round(T / (gres["ms_step"] / 1e3), 1), "unit": "tokens/s",
             "ms_per_step": round(gres["ms_step"], 4),
             "path": "3x short_conv + chunk_fwd_gated (g = lb sigmoid(e^A_log (z + dt_bias)) "
                     "in-kernel, z bf16)",
-            "roofline": {"bound": "hbm", "achieved": round(gach, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gach / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic("gated", args.workload),
-                         "kernel": "kda_chunk_fwd_gated", "algorithmic_bytes_per_launch": gbytes,
-                         "avg_launch_ms": round(gres["chunk_ms"], 4)}}
+            "roofline": chunk_roofline(spec, gres, "kda_chunk_fwd_gated", gated_step_bytes,
+                                       "gated")}
         del gres
     if not args.no_gate:
         hres = run_prefill(args, torch, kda, workloads, gdn=True)
-        hbytes = gdn_step_bytes(T, H, DK, DV, N, spec.h0_std is not None)
-        hach = hbytes / (hres["chunk_ms"] / 1e3) / 1e9
         out["gdn"] = {
             "value": round(T / (hres["ms_step"] / 1e3), 1), "unit": "tokens/s",
             "ms_per_step": round(hres["ms_step"], 4),
             "path": "3x short_conv + gdn_chunk_fwd (one decay per token and head)",
-            "roofline": {"bound": "hbm", "achieved": round(hach, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(hach / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic("gdn", args.workload),
-                         "kernel": "kda_gdn_chunk_fwd",
-                         "algorithmic_bytes_per_launch": hbytes,
-                         "avg_launch_ms": round(hres["chunk_ms"], 4)}}
+            "roofline": chunk_roofline(spec, hres, "kda_gdn_chunk_fwd", gdn_step_bytes, "gdn")}
         del hres
     if not args.no_epilogue:
-        ems = run_epilogue(args, torch, kda, workloads, res["o"])
+        ems = run_epilogue(args, torch, kda, workloads, keep_o)
         ebytes = epilogue_bytes(T, H, DV)
         each = ebytes / (ems / 1e3) / 1e9
         out["output_epilogue"] = {
@@ -438,10 +522,10 @@ def main():
                          "unit": "GB/s", "frac": round(each / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("epilogue", args.workload),
                          "kernel": "norm_gate_kernel", "algorithmic_bytes_per_launch": ebytes}}
-    out["prologue_ms_per_step"] = round(res["ms_step"] - res["chunk_ms"], 4)
+    out["prologue_ms_per_step"] = round(out["ms_per_step"] - roof["avg_launch_ms"], 4)
     out["prologue_bytes_per_step"] = prologue_bytes(T, H, DK)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(res, workloads)
+        out["cpu_baseline"] = cpu_baseline(keep_res, workloads)
     print(json.dumps(out))
 
 

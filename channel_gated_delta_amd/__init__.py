@@ -29,7 +29,7 @@ __all__ = ["KdaError", "library", "short_conv", "chunk_fwd", "chunk_fwd_gated", 
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
-KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP, KDA_ERR_WORKSPACE = 0, 1, 2, 3, 4
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 _lib = None

@@ -92,10 +92,8 @@ kda_status_t chunk_checked_launch(const char *who, const kda::ChunkArgs &a, cons
                                   int mode, size_t workspace_bytes, kda_dtype_t dtype,
                                   kda_dtype_t out_dtype, void *stream) {
     const bool gated = mode == 1;
-    if (a.total_tokens > 0 &&
-        (!a.q || !a.k || !a.v || !gate || !a.beta || !a.o || !a.workspace))
-        return fail(KDA_ERR_INVALID_ARG, "%s: NULL q/k/v/%s/beta/o/workspace", who,
-                    gated ? "z" : "g");
+    if (a.total_tokens > 0 && (!a.q || !a.k || !a.v || !gate || !a.beta || !a.o))
+        return fail(KDA_ERR_INVALID_ARG, "%s: NULL q/k/v/%s/beta/o", who, gated ? "z" : "g");
     if (a.num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "%s: bad sizes", who);
     if (!a.cu_seqlens && a.num_seqs != 1)
         return fail(KDA_ERR_INVALID_ARG, "%s: cu_seqlens NULL needs num_seqs == 1", who);
@@ -113,9 +111,10 @@ kda_status_t chunk_checked_launch(const char *who, const kda::ChunkArgs &a, cons
     if ((int64_t)a.num_seqs * a.heads * (a.dv / 16) > ((int64_t)1 << 28) ||
         (a.total_tokens + c - 1) / c > ((int64_t)1 << 31) - 1)
         return fail(KDA_ERR_UNSUPPORTED, "%s: grid too large", who);
-    if (a.total_tokens > 0 && workspace_bytes < kda::chunk_workspace_bytes(a.total_tokens, a.heads, c))
-        return fail(KDA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", who,
-                    workspace_bytes, kda::chunk_workspace_bytes(a.total_tokens, a.heads, c));
+    const size_t need = kda::chunk_workspace_bytes(a.total_tokens, a.heads, c);
+    if (a.total_tokens > 0 && (!a.workspace || workspace_bytes < need))
+        return fail(KDA_ERR_WORKSPACE, "%s: workspace %s of %zu bytes, %zu needed", who,
+                    a.workspace ? "" : "(NULL)", workspace_bytes, need);
     int used = 0;
     return from_hip(chunk_launcher(dtype, out_dtype, mode)(a, (hipStream_t)stream, true, &used),
                     who);
@@ -156,6 +155,7 @@ KDA_API const char *kda_status_string(kda_status_t s) {
         case KDA_ERR_INVALID_ARG: return "invalid argument";
         case KDA_ERR_UNSUPPORTED: return "unsupported shape, dtype or gate bound";
         case KDA_ERR_HIP: return "HIP runtime error";
+        case KDA_ERR_WORKSPACE: return "workspace missing or too small";
     }
     return "unknown status";
 }

@@ -1,5 +1,5 @@
 // kda_chunk_dispatch.cuh -- host-side choice of the chunk kernel instantiations
-// (internal chunk C, value-slice width BV) for one operand dtype, and the two
+// (value-slice width BV; the internal chunk is 16 tokens) for one operand dtype, and the two
 // launches: the parallel prep kernel (Tb, scale * P for every chunk and head)
 // followed by the sequential state kernel.
 #pragma once
@@ -27,17 +27,11 @@ inline int pick_bv(int dv) {
     return dv % 64 == 0 ? 64 : (dv % 32 == 0 ? 32 : 16);
 }
 
-// Internal chunk: the largest of 64, 32, 16 that is not above the requested size
-// nor the preferred maximum (KDA_CHUNK_MAX) and whose working sets fit in LDS.
-#ifndef KDA_CHUNK_MAX
-#define KDA_CHUNK_MAX 16
-#endif
+// Internal chunk: 16 tokens for every requested chunk size (0 when the working
+// sets do not fit).  The result does not depend on the chunking beyond rounding.
 template <class T, int DK>
-int pick_chunk(int chunk) {
-    if (chunk >= 64 && KDA_CHUNK_MAX >= 64 && fits<T, DK, 64, 64>()) return 64;
-    if (chunk >= 32 && KDA_CHUNK_MAX >= 32 && fits<T, DK, 64, 32>()) return 32;
-    if (chunk >= 16 && fits<T, DK, 64, 16>()) return 16;
-    return 0;
+int pick_chunk(int) {
+    return fits<T, DK, 64, kChunk>() ? kChunk : 0;
 }
 
 template <class T, class TO, int DK, int BV, int C, int GM>
@@ -50,7 +44,7 @@ hipError_t run(const ChunkArgs &a, hipStream_t s) {
         float *pm = tb ? tb + (size_t)a.total_tokens * a.heads * C : nullptr;
         if (a.total_tokens > 0) {
             const int64_t ntiles = (a.total_tokens + C - 1) / C;
-            if constexpr (std::is_same<T, bf16>::value && C == 16 && DK % 32 == 0) {
+            if constexpr (std::is_same<T, bf16>::value && DK % 32 == 0) {
                 // one wave per (tile, head), four per workgroup
                 const int64_t units = ntiles * a.heads;
                 hipLaunchKernelGGL((chunk_prep16_kernel<DK, GM>), dim3((unsigned)((units + 3) / 4)),
@@ -94,15 +88,7 @@ hipError_t run_dk(const ChunkArgs &a, hipStream_t s, bool launch, int *chunk_use
     *chunk_used = c;
     if (c == 0) return hipErrorNotSupported;
     if (!launch) return hipSuccess;
-    switch (c) {
-#if KDA_CHUNK_MAX >= 64
-        case 64: return run_bv<T, TO, DK, 64, GM>(a, s);
-#endif
-#if KDA_CHUNK_MAX >= 32
-        case 32: return run_bv<T, TO, DK, 32, GM>(a, s);
-#endif
-        default: return run_bv<T, TO, DK, 16, GM>(a, s);
-    }
+    return run_bv<T, TO, DK, kChunk, GM>(a, s);
 }
 
 // GM: the gate mode (kGatePlain, kGateFused: ChunkArgs::gz and friends, kGateHead: g [T, H]).

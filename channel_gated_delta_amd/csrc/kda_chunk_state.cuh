@@ -36,7 +36,8 @@ struct StateCfg {
     static constexpr int NSPLIT = kSplit ? 2 : 1;
     // producer waves (KDA_STATE_NPW for dk >= 64 and 16-token chunks), threads: 4
     // consumer waves + producers
-    static constexpr int NPW = (DK >= 64 && C == 16) ? KDA_STATE_NPW : 4;
+    static_assert(C == 16, "chunks are 16 tokens");
+    static constexpr int NPW = DK >= 64 ? KDA_STATE_NPW : 4;
     static constexpr int NT = (4 + NPW) * kWave;
     static constexpr int NTC = C / 16, NTK = DK / 16, NCW = BV / 16;
     // Row pitch padding (elements).  For bf16 the pitches come out at 2 (mod 32)
@@ -99,47 +100,33 @@ __device__ __forceinline__ BReg4 low_half(const BReg8 &b) {
     return r;
 }
 
-// The state chain of one chunk for one consumer wave, bf16 operands, dk a
-// multiple of 32 and chunks of 16 or 32 tokens.  Written as explicit stages
-// whose LDS fragment loads are issued one stage ahead of the products that use
-// them (scheduling barriers keep the compiler from sinking the loads next to
-// their first use, which would expose the LDS latency at every product).
-template <int DK, int C, int LDK, int LDC, int LDV>
+// The state chain of one 16-token chunk for one consumer wave, bf16 operands and
+// dk a multiple of 32.  Written as explicit stages whose LDS fragment loads are
+// issued one stage ahead of the products that use them (scheduling barriers keep
+// the compiler from sinking the loads next to their first use, which would
+// expose the LDS latency at every product).
+template <int DK, int LDK, int LDC, int LDV>
 __device__ __forceinline__ void state_chain_bf16(
-    f32x4 (&Sacc)[DK / 16], BReg8 (&sb)[DK / 32], f32x4 (&Ot)[C / 16], const bf16 *sQdh, const bf16 *sQdl,
+    f32x4 (&Sacc)[DK / 16], BReg8 (&sb)[DK / 32], f32x4 &Ot, const bf16 *sQdh, const bf16 *sQdl,
     const bf16 *sKdh, const bf16 *sKdl, const bf16 *sKrTh, const bf16 *sKrTl, const bf16 *sTbh,
     const bf16 *sTbl, const bf16 *sPh, const bf16 *sPl, const float *sV, const float *sEGn,
     float scale, int wcol, int lane) {
-    constexpr int NTK = DK / 16, NKB = DK / 32, NTC = C / 16;
-    static_assert(DK % 32 == 0 && (C == 16 || C == 32), "shape");
+    constexpr int NTK = DK / 16, NKB = DK / 32;
+    static_assert(DK % 32 == 0, "shape");
     // small operands first: Tb / P fragments and V
     const AF4 tb0 = lda4(sTbh, sTbl, LDC, 0, 0, lane), p0 = lda4(sPh, sPl, LDC, 0, 0, lane);
-    AF8 tb1, p1;
-    if constexpr (NTC == 2) {
-        tb1 = lda8(sTbh, sTbl, LDC, 16, 0, lane);
-        p1 = lda8(sPh, sPl, LDC, 16, 0, lane);
-    }
-    float vin[NTC][4];
+    float vin[4];
 #pragma unroll
-    for (int R = 0; R < NTC; ++R)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vin[R][r] = sV[(R * 16 + acc_row(lane, r)) * LDV + wcol + (lane & 15)];
-    AF8 fk[2][NTC], fq[2][NTC];
-#pragma unroll
-    for (int R = 0; R < NTC; ++R) {
-        fk[0][R] = lda8(sKdh, sKdl, LDK, R * 16, 0, lane);
-        fq[0][R] = lda8(sQdh, sQdl, LDK, R * 16, 0, lane);
-    }
+    for (int r = 0; r < 4; ++r) vin[r] = sV[acc_row(lane, r) * LDV + wcol + (lane & 15)];
+    AF8 fk[2], fq[2];
+    fk[0] = lda8(sKdh, sKdl, LDK, 0, 0, lane);
+    fq[0] = lda8(sQdh, sQdl, LDK, 0, 0, lane);
 
     // E = Kd S, O = Qd S: k-block j's products while block j+1 loads.  The three
     // split terms accumulate in place (an MFMA that depends on the one before it
     // issues at the same rate), E and O products alternating.
-    f32x4 Et[NTC];
-#pragma unroll
-    for (int R = 0; R < NTC; ++R) {
-        Et[R] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Ot[R] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    f32x4 Et = f32x4{0.f, 0.f, 0.f, 0.f};
+    Ot = f32x4{0.f, 0.f, 0.f, 0.f};
     // The state is split into (hi, lo) B operands here, block by block: block j+1's
     // split runs beside block j's products instead of after the previous update.
     sb[0] = breg8(Sacc[0], Sacc[1]);
@@ -147,67 +134,39 @@ __device__ __forceinline__ void state_chain_bf16(
     for (int j = 0; j < NKB; ++j) {
         const int cur = j & 1, nxt = cur ^ 1;
         if (j + 1 < NKB) {
-#pragma unroll
-            for (int R = 0; R < NTC; ++R) {
-                fk[nxt][R] = lda8(sKdh, sKdl, LDK, R * 16, 32 * (j + 1), lane);
-                fq[nxt][R] = lda8(sQdh, sQdl, LDK, R * 16, 32 * (j + 1), lane);
-            }
+            fk[nxt] = lda8(sKdh, sKdl, LDK, 0, 32 * (j + 1), lane);
+            fq[nxt] = lda8(sQdh, sQdl, LDK, 0, 32 * (j + 1), lane);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (j + 1 < NKB) sb[j + 1] = breg8(Sacc[2 * j + 2], Sacc[2 * j + 3]);
-#pragma unroll
-        for (int R = 0; R < NTC; ++R) {
-            Et[R] = mma(fk[cur][R].h, sb[j].h, Et[R]);
-            Ot[R] = mma(fq[cur][R].h, sb[j].h, Ot[R]);
-            Et[R] = mma(fk[cur][R].h, sb[j].l, Et[R]);
-            Ot[R] = mma(fq[cur][R].h, sb[j].l, Ot[R]);
-            Et[R] = mma(fk[cur][R].l, sb[j].h, Et[R]);
-            Ot[R] = mma(fq[cur][R].l, sb[j].h, Ot[R]);
-        }
+        Et = mma(fk[cur].h, sb[j].h, Et);
+        Ot = mma(fq[cur].h, sb[j].h, Ot);
+        Et = mma(fk[cur].h, sb[j].l, Et);
+        Ot = mma(fq[cur].h, sb[j].l, Ot);
+        Et = mma(fk[cur].l, sb[j].h, Et);
+        Ot = mma(fq[cur].l, sb[j].h, Ot);
         __builtin_amdgcn_sched_barrier(0);
     }
     // first half of the state-update fragments load during the U and P U products
     constexpr int NK1 = NTK / 2;
-    AF8 fr8[NTK];
     AF4 fr4[NTK];
 #pragma unroll
-    for (int rt = 0; rt < NK1; ++rt) {
-        if constexpr (C == 32) fr8[rt] = lda8(sKrTh, sKrTl, LDC, rt * 16, 0, lane);
-        else fr4[rt] = lda4(sKrTh, sKrTl, LDC, rt * 16, 0, lane);
-    }
+    for (int rt = 0; rt < NK1; ++rt) fr4[rt] = lda4(sKrTh, sKrTl, LDC, rt * 16, 0, lane);
     __builtin_amdgcn_sched_barrier(0);
     // E = V - Kd S;  U = Tb E;  O = scale Qd S (the stage holds q e^G unscaled)
 #pragma unroll
-    for (int R = 0; R < NTC; ++R)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            Et[R][r] = vin[R][r] - Et[R][r];
-            Ot[R][r] *= scale;
-        }
-    f32x4 Ut[NTC];
-    BReg8 ub8;
-    BReg4 ub4;
-    if constexpr (NTC == 2) {
-        const BReg8 eb = breg8(Et[0], Et[1]);
-        Ut[0] = mma3(tb0.h, tb0.l, low_half(eb), f32x4{0.f, 0.f, 0.f, 0.f});
-        Ut[1] = mma3(tb1.h, tb1.l, eb, f32x4{0.f, 0.f, 0.f, 0.f});
-        ub8 = breg8(Ut[0], Ut[1]);
-        ub4 = low_half(ub8);
-        Ot[0] = mma3(p0.h, p0.l, ub4, Ot[0]);
-        Ot[1] = mma3(p1.h, p1.l, ub8, Ot[1]);
-    } else {
-        const BReg4 eb = breg4(Et[0]);
-        Ut[0] = mma3(tb0.h, tb0.l, eb, f32x4{0.f, 0.f, 0.f, 0.f});
-        ub4 = breg4(Ut[0]);
-        Ot[0] = mma3(p0.h, p0.l, ub4, Ot[0]);
+    for (int r = 0; r < 4; ++r) {
+        Et[r] = vin[r] - Et[r];
+        Ot[r] *= scale;
     }
+    const BReg4 eb = breg4(Et);
+    const f32x4 Ut = mma3(tb0.h, tb0.l, eb, f32x4{0.f, 0.f, 0.f, 0.f});
+    const BReg4 ub4 = breg4(Ut);
+    Ot = mma3(p0.h, p0.l, ub4, Ot);
     __builtin_amdgcn_sched_barrier(0);
     // second half of the fragments load during the first half's products
 #pragma unroll
-    for (int rt = NK1; rt < NTK; ++rt) {
-        if constexpr (C == 32) fr8[rt] = lda8(sKrTh, sKrTl, LDC, rt * 16, 0, lane);
-        else fr4[rt] = lda4(sKrTh, sKrTl, LDC, rt * 16, 0, lane);
-    }
+    for (int rt = NK1; rt < NTK; ++rt) fr4[rt] = lda4(sKrTh, sKrTl, LDC, rt * 16, 0, lane);
     f32x4 eg[NTK];
 #pragma unroll
     for (int rt = 0; rt < NTK; ++rt)
@@ -218,21 +177,12 @@ __device__ __forceinline__ void state_chain_bf16(
     for (int rt = 0; rt < NTK; ++rt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) Sacc[rt][r] *= eg[rt][r];
-    if constexpr (C == 32) {
 #pragma unroll
-        for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr8[rt].h, ub8.h, Sacc[rt]);
+    for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr4[rt].h, ub4.h, Sacc[rt]);
 #pragma unroll
-        for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr8[rt].h, ub8.l, Sacc[rt]);
+    for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr4[rt].h, ub4.l, Sacc[rt]);
 #pragma unroll
-        for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr8[rt].l, ub8.h, Sacc[rt]);
-    } else {
-#pragma unroll
-        for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr4[rt].h, ub4.h, Sacc[rt]);
-#pragma unroll
-        for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr4[rt].h, ub4.l, Sacc[rt]);
-#pragma unroll
-        for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr4[rt].l, ub4.h, Sacc[rt]);
-    }
+    for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr4[rt].l, ub4.h, Sacc[rt]);
 }
 
 template <class T, class TO, int DK, int BV, int C, int GM>
@@ -530,23 +480,21 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                 const float *sV = reinterpret_cast<const float *>(st + Cfg::oV);
                 const float *sEGn = reinterpret_cast<const float *>(st + Cfg::oEGn);
 
-                if constexpr (SPLIT && DK % 32 == 0 && (C == 16 || C == 32)) {
-                    f32x4 Ot[NTC];
-                    state_chain_bf16<DK, C, LDK, LDC, LDV>(Sacc, sbs, Ot, sQdh, sQdl, sKdh, sKdl,
-                                                           sKrTh, sKrTl, sTbh, sTbl, sPh, sPl, sV,
-                                                           sEGn, scale, wave * 16, lane);
+                if constexpr (SPLIT && DK % 32 == 0) {
+                    f32x4 Ot;
+                    state_chain_bf16<DK, LDK, LDC, LDV>(Sacc, sbs, Ot, sQdh, sQdl, sKdh, sKdl,
+                                                        sKrTh, sKrTl, sTbh, sTbl, sPh, sPl, sV,
+                                                        sEGn, scale, wave * 16, lane);
                     TO *ob = o + (size_t)c0 * rowV + (size_t)h * DV;
                     auto store = [&](bool all) {
 #pragma unroll
-                        for (int R = 0; R < NTC; ++R)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int row = R * 16 + acc_row(lane, r);
-                                if (all || row < nt)
-                                    st_off<TO>(ob, ((uint32_t)row * (uint32_t)rowV + (uint32_t)vc) *
-                                                       (uint32_t)sizeof(TO),
-                                               from_f32<TO>(Ot[R][r]));
-                            }
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = acc_row(lane, r);
+                            if (all || row < nt)
+                                st_off<TO>(ob, ((uint32_t)row * (uint32_t)rowV + (uint32_t)vc) *
+                                                   (uint32_t)sizeof(TO),
+                                           from_f32<TO>(Ot[r]));
+                        }
                     };
                     // whole chunks (all but a sequence's last) store without a row test
                     if (nt == C) store(true);

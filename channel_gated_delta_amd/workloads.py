@@ -84,14 +84,14 @@ class DecodeSpec:
 def standard_specs() -> Dict[str, object]:
     """The five workloads: tiny fp32 check, prefill, decode, varlen, long context."""
     return {
-        "tiny_fp32": PrefillSpec("tiny_fp32 B=1 H=1 T=64 d=16 C=16 fp32", [64], heads=1, dk=16,
+        "tiny_fp32": PrefillSpec("tiny_fp32 B=1 H=1 T=64 d=16 chunk=16 fp32", [64], heads=1, dk=16,
                                  dv=16, chunk=16, dtype=torch.float32, conv=False, scale=1.0,
                                  seed=1),
-        "prefill": PrefillSpec("prefill B=1 T=4096 H=96 d=128 C=64 bf16", [4096], seed=2),
+        "prefill": PrefillSpec("prefill B=1 T=4096 H=96 d=128 bf16", [4096], seed=2),
         "decode": DecodeSpec("decode 64 seq x H=96 d=128, 256 steps bf16"),
-        "varlen": PrefillSpec("varlen 8 seq T=32768 H=96 d=128 C=64 bf16 h0", list(VARLEN_LENGTHS),
+        "varlen": PrefillSpec("varlen 8 seq T=32768 H=96 d=128 bf16 h0", list(VARLEN_LENGTHS),
                               h0_std=0.05, seed=4),
-        "long": PrefillSpec("long B=1 T=131072 H=96 d=128 C=64 bf16 g>=-8", [131072], gate_lb=-8.0,
+        "long": PrefillSpec("long B=1 T=131072 H=96 d=128 bf16 g>=-8", [131072], gate_lb=-8.0,
                             gate_std=2.0, seed=5),
     }
 

@@ -4,6 +4,7 @@
  *
  * Sources (web pages, cited by title and section):
  *   [Walkthrough]   "Kimi K3的线性注意力：从源码看懂KDA如何更新记忆"
+ *   [Replication-1] "KIMIK3轻量化复刻解析，KDA机制如何实现通道级可控遗忘"
  *   [Replication-2] "KimiK3轻量化复刻实现KDA并行解析，Chunkwise并行与状态压缩机制详解"
  *
  * Conventions shared by every entry point
@@ -53,7 +54,8 @@ typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1, /* NULL required pointer, negative size, inconsistent sizes */
     KDA_ERR_UNSUPPORTED = 2, /* valid but not implemented shape / dtype / gate bound */
-    KDA_ERR_HIP = 3          /* the HIP runtime rejected a launch */
+    KDA_ERR_HIP = 3,         /* the HIP runtime rejected a launch */
+    KDA_ERR_WORKSPACE = 4    /* workspace NULL or smaller than the call needs */
 } kda_status_t;
 
 typedef enum {
@@ -136,17 +138,22 @@ KDA_API kda_status_t kda_short_conv(const void *x, const void *weight, const voi
  * inside the floating-point range); it must be in [-9, 0].  g below the
  * promised floor gives unspecified accuracy but no out-of-bounds access.
  * Supported: dk, dv in {16, 32, 64, 128}; chunk_size in {16, 32, 64};
- * |q|, |k| entries below 1e3.  Two kernels run on `stream`: the first computes,
- * for every chunk and head at once, the chunk's Tb and the decayed, scaled
- * in-chunk products scale * P_ti = scale * sum_c q_tc k_ic e^{G_tc - G_ic} (i <= t,
- * G the in-chunk cumulative g), which depend on q, k, g, beta only; the second
- * walks the chunks of every sequence with the state on chip.  The fp32 dtype computes in fp32 throughout; the
- * bf16 dtype runs its products on bf16 matrix cores with fp32 accumulation,
- * keeps the recurrent state in fp32 and gives every product split operands
- * (x = hi + lo, both bf16; three-term products), which keeps the products near
- * fp32 accuracy.  The internal chunk may be smaller than chunk_size (the
- * largest of 64, 32, 16 not above it whose working set fits a CU's 160 KiB of
- * LDS); results do not depend on it beyond rounding.
+ * |q|, |k| entries below 1e3.
+ * Chunking.  chunk_size is the caller's chunk; the kernels always walk 16-token
+ * chunks, whatever chunk_size is (16 tokens keep every in-chunk decay factor
+ * inside fp32 for gates down to -9, and a 16-token step is the shortest serial
+ * step on this GPU).  The result does not depend on the chunking beyond
+ * rounding.  Two kernels run on `stream`: the first computes, for every 16-token
+ * chunk and head at once, the chunk's Tb and the decayed, scaled in-chunk
+ * products scale * P_ti = scale * sum_c q_tc k_ic e^{G_tc - G_ic} (i <= t, G the
+ * in-chunk cumulative g), which depend on q, k, g, beta only, into the workspace;
+ * the second walks the chunks of every sequence with the state on chip.  The
+ * fp32 dtype computes in fp32 throughout; the bf16 dtype runs its products on
+ * bf16 matrix cores with fp32 accumulation, keeps the recurrent state in fp32 and
+ * gives every product split operands (x = hi + lo, both bf16; three-term
+ * products), which keeps the products near fp32 accuracy.
+ * Errors: KDA_ERR_WORKSPACE when workspace is NULL (with tokens) or
+ * workspace_bytes is below kda_chunk_fwd_workspace_size().
  */
 KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, const int32_t *cu_seqlens, int32_t num_seqs,
@@ -187,8 +194,8 @@ KDA_API kda_status_t kda_chunk_fwd_gated(const void *q, const void *k, const voi
 
 /*
  * kda_chunk_fwd_workspace_size -- bytes of device workspace kda_chunk_fwd needs
- * for these sizes (written to *bytes): 2 * total_tokens * num_heads * C * 4,
- * where C is the internal chunk size chosen for (dtype, dk, dv, chunk_size).
+ * for these sizes (written to *bytes): 2 * total_tokens * num_heads * 16 * 4
+ * (one row of Tb and one of scale * P per token and head, 16 fp32 each).
  * Returns the same status kda_chunk_fwd would return for an unsupported shape.
  */
 KDA_API kda_status_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_heads,

@@ -19,12 +19,12 @@ def test_more_than_one_gpu_exits_with_a_message():
     assert r.stdout.strip() == ""
 
 
-def _prefill_tensors(T, H, dk, dv, N, h0, gate):
+def _prefill_tensors(T, H, dk, dv, N, h0, gate, o_bytes=2):
     """Bytes of every tensor one chunk call reads or writes once (bf16 activations)."""
     b = 2 * T * H * dk * 2          # q, k (bf16)
     b += T * H * dv * 2             # v (bf16)
     b += T * H * 4                  # beta (fp32)
-    b += T * H * dv * 4             # o (fp32)
+    b += T * H * dv * o_bytes       # o (bf16 in the roofline's accounting; fp32 as written)
     b += N * H * dk * dv * 4        # final state (fp32)
     if h0:
         b += N * H * dk * dv * 4    # initial state
@@ -41,17 +41,32 @@ def _prefill_tensors(T, H, dk, dv, N, h0, gate):
                                              (32768, 96, 128, 128, 8, True),
                                              (64, 1, 16, 16, 1, False)])
 def test_prefill_byte_counts(T, H, dk, dv, N, h0):
-    assert bench.prefill_step_bytes(T, H, dk, dv, N, h0) == _prefill_tensors(T, H, dk, dv, N, h0, "g")
-    assert bench.gdn_step_bytes(T, H, dk, dv, N, h0) == _prefill_tensors(T, H, dk, dv, N, h0, "head")
-    got = bench.gated_step_bytes(T, H, dk, dv, N, h0)
-    want = _prefill_tensors(T, H, dk, dv, N, h0, "z")
-    # A_log and dt_bias are a few KB per call; the count may leave them out
-    assert abs(got - want) <= H * 4 + H * dk * 4
+    for ob in (2, 4):
+        assert bench.prefill_step_bytes(T, H, dk, dv, N, h0, ob) == \
+            _prefill_tensors(T, H, dk, dv, N, h0, "g", ob)
+        assert bench.gdn_step_bytes(T, H, dk, dv, N, h0, ob) == \
+            _prefill_tensors(T, H, dk, dv, N, h0, "head", ob)
+        got = bench.gated_step_bytes(T, H, dk, dv, N, h0, ob)
+        want = _prefill_tensors(T, H, dk, dv, N, h0, "z", ob)
+        # A_log and dt_bias are a few KB per call; the count may leave them out
+        assert abs(got - want) <= H * 4 + H * dk * 4
 
 
 def test_headline_prefill_bytes():
-    # 1796 B per (token, head) plus 64 KiB of final state per head
-    assert bench.prefill_step_bytes(4096, 96, 128, 128, 1, False) == 4096 * 96 * 1796 + 96 * 65536
+    # 1540 B per (token, head) with o counted as bf16 (the roofline's accounting), 1796 B
+    # with the fp32 o the call writes; plus 64 KiB of final state per head
+    assert bench.prefill_step_bytes(4096, 96, 128, 128, 1, False) == 4096 * 96 * 1540 + 96 * 65536
+    assert bench.prefill_step_bytes(4096, 96, 128, 128, 1, False) == 611844096
+    assert bench.prefill_step_bytes(4096, 96, 128, 128, 1, False, 4) == 4096 * 96 * 1796 + 96 * 65536
+    # the packed and long workloads: 4.945 GB (h0 and hT of 8 sequences) and 19.38 GB
+    assert round(bench.prefill_step_bytes(32768, 96, 128, 128, 8, True) / 1e9, 3) == 4.945
+    assert round(bench.prefill_step_bytes(131072, 96, 128, 128, 1, False) / 1e9, 2) == 19.38
+
+
+def test_useful_flops():
+    # 2 [3 dk dv + (C/2)(3 dk + 2 dv)] = 139264 per (token, head) at d = 128, C = 64
+    assert bench.prefill_useful_flops(1, 1, 128, 128, 64) == 139264
+    assert round(bench.prefill_useful_flops(4096, 96, 128, 128, 64) / 1e9, 2) == 54.76
 
 
 def test_decode_byte_counts():
