@@ -8,6 +8,7 @@ fallback: if libkda.so is missing the calls raise.
     short_conv(x, weight, ...)              -> (y, conv_state)   conv4 + SiLU (+ L2)
     chunk_fwd(q, k, v, g, beta, ...)        -> (o, final_state)  chunkwise prefill
     chunk_fwd_gated(q, k, v, z, beta, ...)  -> (o, final_state)  the same, bounded gate fused
+    chunk_fwd_noalloc(q, k, v, g, beta, out, final_state, ...)   no workspace (static scratch)
     output_norm_gate(o, gate, weight, ...)  -> y                 per-head RMSNorm * sigmoid gate
     gdn_chunk_fwd / gdn_decode_step         one decay per (token, head): g [T, H] / [B, H]
     decode_step(q, k, v, g, beta, state)    -> o                 one recurrent step
@@ -25,7 +26,7 @@ import torch
 
 __all__ = ["KdaError", "library", "short_conv", "chunk_fwd", "chunk_fwd_gated", "decode_step",
            "output_norm_gate", "decode_step_conv", "gdn_chunk_fwd", "gdn_decode_step",
-           "LIB_PATH"]
+           "chunk_fwd_noalloc", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -69,10 +70,14 @@ def library() -> ctypes.CDLL:
         lib.kda_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
                                         _vp, _i32, _i32, _vp]
         lib.kda_gdn_chunk_fwd.argtypes = lib.kda_chunk_fwd.argtypes
+        lib.kda_chunk_fwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32,
+                                              _i32, _i32, _f32, _f32, _vp, _vp, _vp, _i32, _i32,
+                                              _vp]
         lib.kda_gdn_decode_step.argtypes = lib.kda_decode_step.argtypes
         for fn in ("kda_short_conv", "kda_chunk_fwd", "kda_chunk_fwd_gated",
                    "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_output_norm_gate",
-                   "kda_decode_step_conv", "kda_gdn_chunk_fwd", "kda_gdn_decode_step"):
+                   "kda_decode_step_conv", "kda_gdn_chunk_fwd", "kda_gdn_decode_step",
+                   "kda_chunk_fwd_noalloc"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_status_string.restype = ctypes.c_char_p
@@ -177,6 +182,41 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     _dev(g, "g", torch.float32, (T, H, dk))
     return _chunk(q, k, v, g, None, beta, cu_seqlens, scale, gate_lower_bound, chunk_size,
                   initial_state, output_final_state, out, final_state, out_dtype, workspace)
+
+
+def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                      beta: torch.Tensor, out: torch.Tensor, final_state: Optional[torch.Tensor],
+                      *, cu_seqlens: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                      gate_lower_bound: float = -5.0, chunk_size: int = 64,
+                      initial_state: Optional[torch.Tensor] = None) -> None:
+    """``chunk_fwd`` through kda_chunk_fwd_noalloc: no workspace, the library's static
+    device scratch instead (at most 524288 token-heads per call; calls that overlap
+    on one GPU race).  The caller passes the outputs ``out`` [T, H, dv] (fp32, or
+    bf16 with bf16 inputs) and ``final_state`` [N, H, dk, dv] fp32 (or None); this
+    wrapper allocates nothing either."""
+    _dev(q, "q")
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError("q must be bf16 or fp32")
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    _dev(k, "k", dt, (T, H, dk))
+    _dev(v, "v", dt, (T, H, dv))
+    _dev(g, "g", torch.float32, (T, H, dk))
+    _dev(beta, "beta", torch.float32, (T, H))
+    N = _seqs(cu_seqlens, T)
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", torch.float32, (N, H, dk, dv))
+    if final_state is not None:
+        _dev(final_state, "final_state", torch.float32, (N, H, dk, dv))
+    if out.dtype not in _DTYPES:
+        raise ValueError("out must be bf16 or fp32")
+    _dev(out, "out", out.dtype, (T, H, dv))
+    sc = dk ** -0.5 if scale is None else float(scale)
+    _check(library().kda_chunk_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,
+        int(chunk_size), sc, float(gate_lower_bound), _ptr(initial_state), _ptr(final_state),
+        _ptr(out), _DTYPES[dt], _DTYPES[out.dtype], _stream(q)))
 
 
 def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

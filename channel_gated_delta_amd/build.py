@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
 ARCH = "gfx950"
 
-SOURCES = ["kda_api.cpp", "kda_prologue.hip", "kda_decode.hip", "kda_chunk_bf16.hip",
+SOURCES = ["kda_api.cpp", "kda_scratch.hip", "kda_prologue.hip", "kda_decode.hip", "kda_chunk_bf16.hip",
            "kda_chunk_bf16_bf16out.hip", "kda_chunk_f32.hip", "kda_chunk_bf16_gz.hip",
            "kda_chunk_bf16_bf16out_gz.hip", "kda_chunk_f32_gz.hip", "kda_epilogue.hip",
            "kda_chunk_bf16_gdn.hip", "kda_chunk_bf16_bf16out_gdn.hip", "kda_chunk_f32_gdn.hip"]

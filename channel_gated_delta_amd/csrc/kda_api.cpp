@@ -85,12 +85,25 @@ int chunk_shape_check(const char *who, int64_t total_tokens, int32_t num_heads, 
     return c;
 }
 
-// The checks and the launch shared by kda_chunk_fwd, kda_chunk_fwd_gated and
-// kda_gdn_chunk_fwd; `gate` is g, the gate's pre-activation z, or the per-head g
-// (mode 0, 1, 2 as for chunk_launcher).
+kda_status_t scratch_address(const char *who, float **out) {
+    void *p = nullptr;
+    const hipError_t e = kda::scratch_address(&p);
+    if (e == hipErrorInvalidDevice)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: the current device is beyond the %d supported", who,
+                    kda::kScratchMaxDevices);
+    if (e != hipSuccess || !p)
+        return fail(KDA_ERR_HIP, "%s: static scratch address: %s", who, hipGetErrorString(e));
+    *out = static_cast<float *>(p);
+    return KDA_OK;
+}
+
+// The checks and the launch shared by kda_chunk_fwd, kda_chunk_fwd_gated,
+// kda_gdn_chunk_fwd and kda_chunk_fwd_noalloc; `gate` is g, the gate's
+// pre-activation z, or the per-head g (mode 0, 1, 2 as for chunk_launcher).  With
+// use_scratch the workspace is the static `scratch` of the current device.
 kda_status_t chunk_checked_launch(const char *who, const kda::ChunkArgs &a, const void *gate,
                                   int mode, size_t workspace_bytes, kda_dtype_t dtype,
-                                  kda_dtype_t out_dtype, void *stream) {
+                                  kda_dtype_t out_dtype, void *stream, bool use_scratch = false) {
     const bool gated = mode == 1;
     if (a.total_tokens > 0 && (!a.q || !a.k || !a.v || !gate || !a.beta || !a.o))
         return fail(KDA_ERR_INVALID_ARG, "%s: NULL q/k/v/%s/beta/o", who, gated ? "z" : "g");
@@ -112,11 +125,25 @@ kda_status_t chunk_checked_launch(const char *who, const kda::ChunkArgs &a, cons
         (a.total_tokens + c - 1) / c > ((int64_t)1 << 31) - 1)
         return fail(KDA_ERR_UNSUPPORTED, "%s: grid too large", who);
     const size_t need = kda::chunk_workspace_bytes(a.total_tokens, a.heads, c);
-    if (a.total_tokens > 0 && (!a.workspace || workspace_bytes < need))
+    kda::ChunkArgs run = a;
+    if (use_scratch) {
+        if (need > kda::kScratchBytes)
+            return fail(KDA_ERR_UNSUPPORTED,
+                        "%s: %lld tokens x %d heads need %zu bytes of scratch; the static "
+                        "scratch holds %zu (at most %zu token-heads)",
+                        who, (long long)a.total_tokens, a.heads, need, kda::kScratchBytes,
+                        kda::kScratchBytes / kda::chunk_workspace_bytes(1, 1, c));
+        run.workspace = nullptr;
+        if (a.total_tokens > 0) {
+            const kda_status_t s2 = scratch_address(who, &run.workspace);
+            if (s2 != KDA_OK) return s2;
+        }
+    } else if (a.total_tokens > 0 && (!a.workspace || workspace_bytes < need)) {
         return fail(KDA_ERR_WORKSPACE, "%s: workspace %s of %zu bytes, %zu needed", who,
                     a.workspace ? "" : "(NULL)", workspace_bytes, need);
+    }
     int used = 0;
-    return from_hip(chunk_launcher(dtype, out_dtype, mode)(a, (hipStream_t)stream, true, &used),
+    return from_hip(chunk_launcher(dtype, out_dtype, mode)(run, (hipStream_t)stream, true, &used),
                     who);
 }
 
@@ -225,6 +252,22 @@ KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, 
                            (float *)workspace, nullptr, nullptr, nullptr};
     return chunk_checked_launch("kda_chunk_fwd", a, g, 0, workspace_bytes, dtype, out_dtype,
                                 stream);
+}
+
+KDA_API kda_status_t kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                           const float *g, const float *beta,
+                                           const int32_t *cu_seqlens, int32_t num_seqs,
+                                           int64_t total_tokens, int32_t num_heads, int32_t dk,
+                                           int32_t dv, int32_t chunk_size, float scale,
+                                           float gate_lower_bound, const float *initial_state,
+                                           float *final_state, void *o, kda_dtype_t dtype,
+                                           kda_dtype_t out_dtype, void *stream) {
+    g_last_error[0] = '\0';
+    const kda::ChunkArgs a{q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, dk,
+                           dv, chunk_size, scale, gate_lower_bound, initial_state, final_state, o,
+                           nullptr, nullptr, nullptr, nullptr};
+    return chunk_checked_launch("kda_chunk_fwd_noalloc", a, g, 0, 0, dtype, out_dtype, stream,
+                                true);
 }
 
 KDA_API kda_status_t kda_gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g,

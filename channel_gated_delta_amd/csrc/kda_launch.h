@@ -42,6 +42,14 @@ inline size_t chunk_workspace_bytes(int64_t total_tokens, int32_t heads, int c) 
     return (size_t)2 * (size_t)total_tokens * (size_t)heads * (size_t)c * sizeof(float);
 }
 
+// The library's static device scratch (kda_scratch.hip), the workspace of
+// kda_chunk_fwd_noalloc: its size, and its address on the calling thread's
+// current device (looked up once per device; hipErrorInvalidDevice for a device
+// index at or beyond kScratchMaxDevices).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kScratchMaxDevices = 64;
+hipError_t scratch_address(void **ptr);
+
 struct NormGateArgs {
     const void *o, *gate;
     const float *weight;   // [dv] or NULL

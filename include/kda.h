@@ -164,6 +164,32 @@ KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, 
                            kda_dtype_t out_dtype, void *stream);
 
 /*
+ * kda_chunk_fwd_noalloc -- kda_chunk_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation and arguments without the workspace.
+ * The Tb / P rows go to a static device array of the library (64 MiB per GPU,
+ * held from the library's load until the process ends), so the call itself
+ * allocates nothing.  Limit: total_tokens * num_heads <= 524288 (4096 tokens x
+ * 128 heads; the prefill workload's 4096 x 96 fits); a larger call returns
+ * KDA_ERR_UNSUPPORTED and enqueues nothing.  The scratch of a GPU is shared by
+ * every call on it: two such calls that overlap in time on one GPU (different
+ * streams, or threads without ordering) race and give undefined results; calls
+ * ordered on one stream are safe.  The device used is the calling thread's
+ * current HIP device, which must be the device of `stream`.  Its address is
+ * looked up once per device (hipGetSymbolAddress) on the first call there.
+ * Every other argument, the supported shapes and the errors are those of
+ * kda_chunk_fwd.
+ */
+KDA_API kda_status_t kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                           const float *g, const float *beta,
+                                           const int32_t *cu_seqlens, int32_t num_seqs,
+                                           int64_t total_tokens, int32_t num_heads, int32_t dk,
+                                           int32_t dv, int32_t chunk_size, float scale,
+                                           float gate_lower_bound, const float *initial_state,
+                                           float *final_state, void *o, kda_dtype_t dtype,
+                                           kda_dtype_t out_dtype, void *stream);
+
+/*
  * kda_chunk_fwd_gated -- kda_chunk_fwd with the bounded forget gate fused in.
  *
  * Instead of the log-decay g the caller passes the gate's pre-activation z and

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
                           "kda_chunk_fwd_workspace_size", "kda_decode_step",
                           "kda_output_norm_gate", "kda_decode_step_conv", "kda_gdn_chunk_fwd",
                           "kda_gdn_decode_step", "kda_status_string", "kda_last_error",
-                          "kda_version"}
+                          "kda_version", "kda_chunk_fwd_noalloc"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -258,3 +258,29 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 2, 16)
     with pytest.raises(ValueError):
         kda.chunk_fwd(x, x, x, x, x[..., 0])
+
+
+def noalloc(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, cu=NULL, N=1, T=64, H=2, dk=128, dv=128, chunk=64,
+             scale=0.1, lb=-5.0, h0=NULL, hT=NULL, o=ctypes.c_void_p(8192), dtype=BF16, odt=F32)
+    a.update(kw)
+    return lib.kda_chunk_fwd_noalloc(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"],
+                                     a["T"], a["H"], a["dk"], a["dv"], a["chunk"], a["scale"],
+                                     a["lb"], a["h0"], a["hT"], a["o"], a["dtype"], a["odt"], NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), kda.KDA_ERR_INVALID_ARG),
+    (dict(o=P), kda.KDA_ERR_INVALID_ARG),
+    (dict(dk=48), kda.KDA_ERR_UNSUPPORTED),
+    (dict(lb=-9.5), kda.KDA_ERR_UNSUPPORTED),
+    # the static scratch holds 64 MiB: 524288 token-heads of Tb and P rows
+    (dict(T=5462, H=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(T=524289, H=1), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_noalloc_rejects_before_any_device_call(lib, kw, status):
+    """Argument and size checks run on the host before the scratch lookup (no GPU here)."""
+    assert noalloc(lib, **kw) == status
+    assert lib.kda_last_error()
+    if status == kda.KDA_ERR_UNSUPPORTED and "T" in kw:
+        assert b"scratch" in lib.kda_last_error()
