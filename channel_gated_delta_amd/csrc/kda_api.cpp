@@ -122,7 +122,7 @@ kda_status_t chunk_checked_launch(const char *who, const kda::ChunkArgs &a, cons
                                     out_dtype, &st);
     if (c == 0) return st;
     if ((int64_t)a.num_seqs * a.heads * (a.dv / 16) > ((int64_t)1 << 28) ||
-        (a.total_tokens + c - 1) / c > ((int64_t)1 << 31) - 1)
+        a.total_tokens / c >= ((int64_t)1 << 31) - 1)   // tiles of the prep grid
         return fail(KDA_ERR_UNSUPPORTED, "%s: grid too large", who);
     const size_t need = kda::chunk_workspace_bytes(a.total_tokens, a.heads, c);
     kda::ChunkArgs run = a;
@@ -322,7 +322,7 @@ KDA_API kda_status_t kda_output_norm_gate(const void *o, const void *gate, const
     if (!head_dim_ok(dv)) return fail(KDA_ERR_UNSUPPORTED, "kda_output_norm_gate: dv not in {16,32,64,128}");
     if (o_dtype == KDA_DTYPE_BF16 && dtype != KDA_DTYPE_BF16)
         return fail(KDA_ERR_UNSUPPORTED, "kda_output_norm_gate: bf16 o needs a bf16 gate and y");
-    if ((rows * (dv / 4) + 255) / 256 > ((int64_t)1 << 31) - 1)
+    if (rows > ((int64_t)1 << 40) || (rows * (dv / 4) + 255) / 256 > ((int64_t)1 << 31) - 1)
         return fail(KDA_ERR_UNSUPPORTED, "kda_output_norm_gate: grid too large");
     const kda::NormGateArgs a{o, gate, weight, eps, rows, dv, y};
     return from_hip(kda::launch_norm_gate(a, o_dtype == KDA_DTYPE_BF16, dtype == KDA_DTYPE_BF16,

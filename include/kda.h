@@ -50,18 +50,23 @@ extern "C" {
 #define KDA_API __attribute__((visibility("default")))
 #endif
 
-typedef enum {
+/* Status codes and dtypes are plain 32-bit integers with named values (not C
+   enum types), so that any value a caller passes or receives is well defined on
+   both sides of the ABI; out-of-range values are rejected, never undefined. */
+typedef int32_t kda_status_t;
+enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1, /* NULL required pointer, negative size, inconsistent sizes */
     KDA_ERR_UNSUPPORTED = 2, /* valid but not implemented shape / dtype / gate bound */
     KDA_ERR_HIP = 3,         /* the HIP runtime rejected a launch */
     KDA_ERR_WORKSPACE = 4    /* workspace NULL or smaller than the call needs */
-} kda_status_t;
+};
 
-typedef enum {
+typedef int32_t kda_dtype_t;
+enum {
     KDA_DTYPE_F32 = 0,
     KDA_DTYPE_BF16 = 1
-} kda_dtype_t;
+};
 
 /*
  * kda_short_conv -- causal depthwise convolution + SiLU, optionally followed by
