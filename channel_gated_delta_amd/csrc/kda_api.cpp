@@ -132,7 +132,7 @@ kda_status_t chunk_checked_launch(const char *who, const kda::ChunkArgs &a, cons
                         "%s: %lld tokens x %d heads need %zu bytes of scratch; the static "
                         "scratch holds %zu (at most %zu token-heads)",
                         who, (long long)a.total_tokens, a.heads, need, kda::kScratchBytes,
-                        kda::kScratchBytes / kda::chunk_workspace_bytes(1, 1, c));
+                        (kda::kScratchBytes - kda::kOrderBytes) / (2 * sizeof(float) * c));
         run.workspace = nullptr;
         if (a.total_tokens > 0) {
             const kda_status_t s2 = scratch_address(who, &run.workspace);

@@ -92,6 +92,31 @@ __device__ __forceinline__ int64_t chunk_seq_off(const int32_t *cu, int i, int64
     return min((int64_t)max(cu[i], 0), total);
 }
 
+// Dispatch order of a packed batch for the state kernel: every sequence's rank
+// by decreasing length (ties: lower index first), stored as order[rank] = n.
+// With the longest sequences dispatched first, the state kernel's last
+// workgroups are short ones (list scheduling, longest job first).  The ranks
+// form a permutation of 0 .. nseq-1 for any offsets (the order is strict), so
+// every entry of `order` is written exactly once.  MAXSEQ bounds nseq (the host
+// launches it only for batches that fit).
+template <int MAXSEQ>
+__global__ __launch_bounds__(256) void seq_order_kernel(const int32_t *__restrict__ cu, int nseq,
+                                                        int64_t total, int32_t *__restrict__ order) {
+    __shared__ int64_t len[MAXSEQ];
+    if (nseq > MAXSEQ) return;
+    for (int i = threadIdx.x; i < nseq; i += 256) {
+        const int64_t b = chunk_seq_off(cu, i, total);
+        len[i] = max(chunk_seq_off(cu, i + 1, total), b) - b;
+    }
+    __syncthreads();
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    if (n >= nseq) return;
+    const int64_t ln = len[n];
+    int rank = 0;
+    for (int m = 0; m < nseq; ++m) rank += (len[m] > ln) | ((len[m] == ln) & (m < n));
+    order[rank] = n;
+}
+
 __device__ __forceinline__ void split2(float x, bf16 &hh, bf16 &ll) {
     hh = (bf16)x;
     ll = (bf16)(x - (float)hh);

@@ -42,6 +42,15 @@ hipError_t run(const ChunkArgs &a, hipStream_t s) {
         float *tb = a.workspace;
         const GateSrc gs{a.g, a.gz, a.a_log, a.dt_bias, a.gate_lb};
         float *pm = tb ? tb + (size_t)a.total_tokens * a.heads * C : nullptr;
+        int32_t *order = nullptr;
+        if (a.total_tokens > 0 && a.cu_seqlens && a.num_seqs > 1 && a.num_seqs <= kOrderMaxSeqs) {
+            order = reinterpret_cast<int32_t *>(pm + (size_t)a.total_tokens * a.heads * C);
+            hipLaunchKernelGGL(seq_order_kernel<kOrderMaxSeqs>,
+                               dim3((unsigned)((a.num_seqs + 255) / 256)),
+                               dim3(256), 0, s, a.cu_seqlens, a.num_seqs, a.total_tokens, order);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
         if (a.total_tokens > 0) {
             const int64_t ntiles = (a.total_tokens + C - 1) / C;
             if constexpr (std::is_same<T, bf16>::value && DK % 32 == 0) {
@@ -68,7 +77,7 @@ hipError_t run(const ChunkArgs &a, hipStream_t s) {
                            dim3(StateCfg<T, DK, BV, C>::NT), 0, s,
                            (const T *)a.q, (const T *)a.k, (const T *)a.v, gs, tb, pm,
                            a.cu_seqlens, a.total_tokens, a.heads, a.dv, a.scale, a.h0, a.hT,
-                           (TO *)a.o, units, nslice);
+                           (TO *)a.o, units, nslice, order);
         return hipGetLastError();
     }
 }

@@ -191,7 +191,8 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                         GateSrc gs, const float *__restrict__ tb,
                         const float *__restrict__ pm, const int32_t *__restrict__ cu_seqlens,
                         int64_t total, int H, int DV, float scale, const float *__restrict__ h0,
-                        float *__restrict__ hT, TO *__restrict__ o, int units, int nslice) {
+                        float *__restrict__ hT, TO *__restrict__ o, int units, int nslice,
+                        const int32_t *__restrict__ order) {
     using Cfg = StateCfg<T, DK, BV, C>;
     constexpr bool SPLIT = Cfg::kSplit;
     constexpr int NTC = Cfg::NTC, NTK = Cfg::NTK, NCW = Cfg::NCW;
@@ -211,9 +212,11 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
     // in that XCD's L2.
     const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
     const int slice = slot % nslice;
-    const int unit = (slot / nslice) * 8 + xcd;
-    if (unit >= units) return;
-    const int n = unit / H, h = unit % H;
+    const int pos = (slot / nslice) * 8 + xcd;    // position in the dispatch order
+    if (pos >= units) return;
+    // Packed batches (given `order`) take their sequences longest first.
+    const int n = order ? order[pos / H] : pos / H, h = pos % H;
+    const int unit = n * H + h;
     const int64_t bos = chunk_seq_off(cu_seqlens, n, total);
     const int64_t eos = max(chunk_seq_off(cu_seqlens, n + 1, total), bos);
     const int nchunks = (int)((eos - bos + C - 1) / C);

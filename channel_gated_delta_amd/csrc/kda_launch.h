@@ -37,16 +37,25 @@ struct ChunkArgs {
     const float *a_log, *dt_bias;
 };
 
-// Workspace of the chunk prefill for internal chunk c: Tb and scale * P rows.
+// Packed batches of up to kOrderMaxSeqs sequences run their longest sequences
+// first: the state kernel's dispatch order, order[rank] = sequence, sits after
+// the Tb and P rows in the workspace.
+constexpr int kOrderMaxSeqs = 1024;
+constexpr size_t kOrderBytes = (size_t)kOrderMaxSeqs * sizeof(int32_t);
+
+// Workspace of the chunk prefill for internal chunk c: Tb and scale * P rows and
+// the dispatch order (nothing without tokens).
 inline size_t chunk_workspace_bytes(int64_t total_tokens, int32_t heads, int c) {
-    return (size_t)2 * (size_t)total_tokens * (size_t)heads * (size_t)c * sizeof(float);
+    if (total_tokens <= 0) return 0;
+    return (size_t)2 * (size_t)total_tokens * (size_t)heads * (size_t)c * sizeof(float) +
+           kOrderBytes;
 }
 
 // The library's static device scratch (kda_scratch.hip), the workspace of
 // kda_chunk_fwd_noalloc: its size, and its address on the calling thread's
 // current device (looked up once per device; hipErrorInvalidDevice for a device
 // index at or beyond kScratchMaxDevices).
-constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr size_t kScratchBytes = ((size_t)64 << 20) + kOrderBytes;
 constexpr int kScratchMaxDevices = 64;
 hipError_t scratch_address(void **ptr);
 

@@ -152,7 +152,8 @@ KDA_API kda_status_t kda_short_conv(const void *x, const void *weight, const voi
  * chunk and head at once, the chunk's Tb and the decayed, scaled in-chunk
  * products scale * P_ti = scale * sum_c q_tc k_ic e^{G_tc - G_ic} (i <= t, G the
  * in-chunk cumulative g), which depend on q, k, g, beta only, into the workspace;
- * the second walks the chunks of every sequence with the state on chip.  The
+ * the second walks the chunks of every sequence with the state on chip, the
+ * sequences of a packed batch (up to 1024 of them) longest first.  The
  * fp32 dtype computes in fp32 throughout; the bf16 dtype runs its products on
  * bf16 matrix cores with fp32 accumulation, keeps the recurrent state in fp32 and
  * gives every product split operands (x = hi + lo, both bf16; three-term
@@ -225,8 +226,10 @@ KDA_API kda_status_t kda_chunk_fwd_gated(const void *q, const void *k, const voi
 
 /*
  * kda_chunk_fwd_workspace_size -- bytes of device workspace kda_chunk_fwd needs
- * for these sizes (written to *bytes): 2 * total_tokens * num_heads * 16 * 4
- * (one row of Tb and one of scale * P per token and head, 16 fp32 each).
+ * for these sizes (written to *bytes): 2 * total_tokens * num_heads * 16 * 4 + 4096
+ * (one row of Tb and one of scale * P per token and head, 16 fp32 each, and the
+ * order in which a packed batch of up to 1024 sequences is walked: longest
+ * first), or 0 without tokens.
  * Returns the same status kda_chunk_fwd would return for an unsupported shape.
  */
 KDA_API kda_status_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_heads,

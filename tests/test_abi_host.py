@@ -73,11 +73,13 @@ def ws_size(lib, T=64, H=2, dk=128, dv=128, chunk=64, dtype=BF16, odt=F32):
 
 
 def test_workspace_size(lib):
-    # two fp32 rows of the internal 16-token chunk per token and head
-    assert ws_size(lib) == (kda.KDA_OK, 2 * 64 * 2 * 16 * 4)
-    assert ws_size(lib, chunk=16) == (kda.KDA_OK, 2 * 64 * 2 * 16 * 4)
+    # two fp32 rows of the internal 16-token chunk per token and head, and 4 KiB of
+    # dispatch order for packed batches
+    assert ws_size(lib) == (kda.KDA_OK, 2 * 64 * 2 * 16 * 4 + 4096)
+    assert ws_size(lib, chunk=16) == (kda.KDA_OK, 2 * 64 * 2 * 16 * 4 + 4096)
     assert ws_size(lib, T=0) == (kda.KDA_OK, 0)
-    assert ws_size(lib, dtype=F32, dk=16, dv=16, chunk=32) == (kda.KDA_OK, 2 * 64 * 2 * 16 * 4)
+    assert ws_size(lib, dtype=F32, dk=16, dv=16, chunk=32) == \
+        (kda.KDA_OK, 2 * 64 * 2 * 16 * 4 + 4096)
     assert ws_size(lib, dk=48)[0] == kda.KDA_ERR_UNSUPPORTED
     assert ws_size(lib, chunk=8)[0] == kda.KDA_ERR_UNSUPPORTED
     assert ws_size(lib, dtype=F32, odt=BF16)[0] == kda.KDA_ERR_UNSUPPORTED
@@ -106,7 +108,7 @@ def test_workspace_size(lib):
     (dict(chunk=128), kda.KDA_ERR_UNSUPPORTED),
     (dict(chunk=8), kda.KDA_ERR_UNSUPPORTED),
     (dict(ws=NULL), kda.KDA_ERR_WORKSPACE),
-    (dict(wsb=2 * 64 * 2 * 16 * 4 - 1), kda.KDA_ERR_WORKSPACE),     # one byte short
+    (dict(wsb=2 * 64 * 2 * 16 * 4 + 4096 - 1), kda.KDA_ERR_WORKSPACE),   # one byte short
     (dict(o=ctypes.c_void_p(1 << 20)), kda.KDA_ERR_INVALID_ARG),     # o aliases the workspace
 ])
 def test_chunk_fwd_rejects(lib, kw, status):
@@ -119,7 +121,7 @@ def test_chunk_fwd_rejects(lib, kw, status):
     (dict(o=P), kda.KDA_ERR_INVALID_ARG),
     (dict(lb=-9.5), kda.KDA_ERR_UNSUPPORTED),
     (dict(dk=48), kda.KDA_ERR_UNSUPPORTED),
-    (dict(wsb=2 * 64 * 2 * 16 * 4 - 1), kda.KDA_ERR_WORKSPACE),
+    (dict(wsb=2 * 64 * 2 * 16 * 4 + 4096 - 1), kda.KDA_ERR_WORKSPACE),
 ])
 def test_gdn_calls_reject(lib, kw, status):
     a = dict(q=P, k=P, v=P, g=P, beta=P, cu=NULL, N=1, T=64, H=2, dk=128, dv=128, chunk=64,
@@ -160,7 +162,7 @@ def chunk_gated(lib, **kw):
     (dict(lb=-9.5), kda.KDA_ERR_UNSUPPORTED),
     (dict(dk=48), kda.KDA_ERR_UNSUPPORTED),
     (dict(dtype=F32, odt=BF16), kda.KDA_ERR_UNSUPPORTED),
-    (dict(wsb=2 * 64 * 2 * 16 * 4 - 1), kda.KDA_ERR_WORKSPACE),
+    (dict(wsb=2 * 64 * 2 * 16 * 4 + 4096 - 1), kda.KDA_ERR_WORKSPACE),
     (dict(N=2), kda.KDA_ERR_INVALID_ARG),
 ])
 def test_chunk_fwd_gated_rejects(lib, kw, status):

@@ -111,6 +111,19 @@ def test_empty_and_single_token_sequences():
     check_prefill(spec)
 
 
+@pytest.mark.parametrize("nseq", [300, 1100])
+def test_many_packed_sequences(nseq):
+    """Hundreds of packed sequences with ties and empty ones: 300 are walked longest
+    first (the order kernel spans two blocks), 1100 exceed the ordered batches' cap
+    and keep their packed order.  Random h0 checks that every sequence's state
+    lands in its own slot."""
+    rng = np.random.default_rng(nseq)
+    lengths = [int(x) for x in rng.integers(0, 40, size=nseq)]
+    lengths[nseq // 2] = 200                      # the longest sits in the middle
+    note("%d packed sequences, %d tokens" % (nseq, sum(lengths)))
+    check_prefill(spec_of(lengths, H=2, h0=0.05, seed=nseq))
+
+
 def test_zero_tokens():
     spec = spec_of([0], H=2, h0=0.05, seed=7)
     inp = workloads.make_prefill(spec, DEV)
