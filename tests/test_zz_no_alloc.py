@@ -1,7 +1,8 @@
 """kda_chunk_fwd_noalloc (static device scratch, no workspace) against kda_chunk_fwd
 (caller workspace) on the GPU: two calls in a row, the second smaller, each
 bit-identical to the workspace entry point's result on the same inputs (same
-kernels, same arithmetic), and a call beyond the scratch's limit refused."""
+kernels, same arithmetic), for bf16 and fp32 inputs; and a call beyond the
+scratch's limit refused."""
 import pytest
 import torch
 
@@ -34,10 +35,12 @@ def no_alloc(inp, spec):
     return o, hT
 
 
-def test_no_alloc_matches_workspace_entry_point():
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_no_alloc_matches_workspace_entry_point(dtype):
     big = workloads.PrefillSpec("big", [2048, 1000, 1048], heads=96, conv=False, h0_std=0.05,
-                                seed=91)
-    small = workloads.PrefillSpec("small", [37, 200], heads=8, conv=False, h0_std=0.05, seed=92)
+                                dtype=dtype, seed=91)
+    small = workloads.PrefillSpec("small", [37, 200], heads=8, conv=False, h0_std=0.05,
+                                  dtype=dtype, seed=92)
     for spec in (big, small):
         note("no-alloc chunk call: %d tokens x %d heads" % (spec.total_tokens, spec.heads))
         inp = workloads.make_prefill(spec, DEV)
@@ -52,7 +55,9 @@ def test_no_alloc_matches_workspace_entry_point():
 
 
 def test_no_alloc_refuses_beyond_the_scratch():
-    spec = workloads.PrefillSpec("over", [5462], heads=96, conv=False, seed=93)  # 524352 > 524288
+    # Tb / P rows of 5462 x 96 = 524352 token-heads: above the scratch's 524288
+    spec = workloads.PrefillSpec("over", [5462], heads=96, conv=False, dtype=torch.float32,
+                                 seed=93)
     inp = workloads.make_prefill(spec, DEV)
     o = torch.full((spec.total_tokens, 96, 128), float("nan"), device=DEV)
     with pytest.raises(kda.KdaError) as e:
