@@ -273,15 +273,15 @@ __device__ __forceinline__ void afrag4(const bf16 *Mh, const bf16 *Ml, int ld, i
 
 __device__ __forceinline__ f32x4 mma3(const bf16x8 &ah, const bf16x8 &al, const BReg8 &bb,
                                       f32x4 c) {
-    c = mma(ah, bb.h, c);
-    c = mma(ah, bb.l, c);
-    return mma(al, bb.h, c);
+    c = mma_sep(ah, bb.h, c);
+    c = mma_sep(ah, bb.l, c);
+    return mma_sep(al, bb.h, c);
 }
 __device__ __forceinline__ f32x4 mma3(const bf16x4 &ah, const bf16x4 &al, const BReg4 &bb,
                                       f32x4 c) {
-    c = mma(ah, bb.h, c);
-    c = mma(ah, bb.l, c);
-    return mma(al, bb.h, c);
+    c = mma_sep(ah, bb.h, c);
+    c = mma_sep(ah, bb.l, c);
+    return mma_sep(al, bb.h, c);
 }
 
 // D += A[row0.., 0..16*nb) * B, with B given as NBLK 16-row accumulator tiles

@@ -221,13 +221,13 @@ void chunk_prep_kernel(const T *__restrict__ q, const T *__restrict__ k, GateSrc
                     auto kl = load_frag<T, KPL_DK>(sKDl, LDK, 0, k0, lane);
                     auto ql = load_frag<T, KPL_DK>(sQDl, LDK, 0, k0, lane);
                     auto cl = load_frag<T, KPL_DK>(sKCl, LDK, 0, k0, lane);
-                    accA = mma(kh, cl, accA);
-                    accA = mma(kl, ch, accA);
-                    accP = mma(qh, cl, accP);
-                    accP = mma(ql, ch, accP);
+                    accA = mma_sep(kh, cl, accA);
+                    accA = mma_sep(kl, ch, accA);
+                    accP = mma_sep(qh, cl, accP);
+                    accP = mma_sep(ql, ch, accP);
                 }
-                accA = mma(kh, ch, accA);
-                accP = mma(qh, ch, accP);
+                accA = mma_sep(kh, ch, accA);
+                accP = mma_sep(qh, ch, accP);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {

@@ -60,16 +60,26 @@ struct StateCfg {
     static_assert(CPW >= 1 && RG * RP == C && NCW <= 4 && BV % 16 == 0, "shape");
     static_assert(NTB >= 1 && (NTB == 1 || NTB % 4 == 0) && NVE >= 1, "shape");
 
+    // bf16 with dk a multiple of 32 (the register-B chain below): the 16-deep
+    // operands (Kr^T, Tb, P) hold hi and lo interleaved by
+    // 4-token group -- group g of a row is hi[4g..4g+3] then lo[4g..4g+3] -- so one
+    // 16-byte read is the [hi | lo] operand of a 16x16x32 product.  The pitch, 2C + 8
+    // elements (20 dwords), puts 8 consecutive rows on distinct banks.
+    static constexpr int LDG = 2 * C + 8;
+    static constexpr bool kIL = kSplit && DK % 32 == 0;   // the register-B chain's layout
+
     static constexpr size_t al(size_t x) { return (x + 15) & ~(size_t)15; }
     static constexpr size_t szCK = al((size_t)C * LDK * sizeof(T));      // [C][DK]
     static constexpr size_t szKC = al((size_t)DK * LDC * sizeof(T));     // [DK][C]
     static constexpr size_t szCC = al((size_t)C * LDC * sizeof(T));      // [C][C]
+    static constexpr size_t szKrT = kIL ? al((size_t)DK * LDG * sizeof(T)) : NSPLIT * szKC;
+    static constexpr size_t szTbP = kIL ? al((size_t)C * LDG * sizeof(T)) : NSPLIT * szCC;
     static constexpr size_t oQd = 0;                                // q e^G (hi, lo)
     static constexpr size_t oKd = oQd + NSPLIT * szCK;              // k e^G (hi, lo)
-    static constexpr size_t oKrT = oKd + NSPLIT * szCK;             // (k e^{Gn-G})^T (hi, lo)
-    static constexpr size_t oTb = oKrT + NSPLIT * szKC;             // Tb (hi, lo)
-    static constexpr size_t oP = oTb + NSPLIT * szCC;               // scale * P (hi, lo)
-    static constexpr size_t oV = oP + NSPLIT * szCC;                // V (fp32)
+    static constexpr size_t oKrT = oKd + NSPLIT * szCK;             // (k e^{Gn-G})^T
+    static constexpr size_t oTb = oKrT + szKrT;                     // Tb
+    static constexpr size_t oP = oTb + szTbP;                       // scale * P
+    static constexpr size_t oV = oP + szTbP;                        // V (fp32)
     static constexpr size_t oEGn = oV + al((size_t)C * LDV * 4);    // e^{G_n}
     static constexpr size_t kStage = oEGn + al((size_t)DK * 4);
     static constexpr size_t kLds = 2 * kStage;
@@ -78,7 +88,6 @@ struct StateCfg {
 
 // A fragments (hi, lo) in the permuted k order of the register-B products.
 struct AF8 { bf16x8 h, l; };
-struct AF4 { bf16x4 h, l; };
 
 __device__ __forceinline__ AF8 lda8(const bf16 *Mh, const bf16 *Ml, int ld, int row0, int k0,
                                     int lane) {
@@ -86,35 +95,44 @@ __device__ __forceinline__ AF8 lda8(const bf16 *Mh, const bf16 *Ml, int ld, int 
     afrag8(Mh, Ml, ld, row0, k0, lane, f.h, f.l);
     return f;
 }
-__device__ __forceinline__ AF4 lda4(const bf16 *Mh, const bf16 *Ml, int ld, int row0, int k0,
-                                    int lane) {
-    AF4 f;
-    afrag4(Mh, Ml, ld, row0, k0, lane, f.h, f.l);
-    return f;
-}
-__device__ __forceinline__ BReg4 low_half(const BReg8 &b) {
-    const u32x4 h = __builtin_bit_cast(u32x4, b.h), l = __builtin_bit_cast(u32x4, b.l);
-    BReg4 r;
-    r.h = __builtin_bit_cast(bf16x4, u32x2{h[0], h[1]});
-    r.l = __builtin_bit_cast(bf16x4, u32x2{l[0], l[1]});
-    return r;
-}
 
 // The state chain of one 16-token chunk for one consumer wave, bf16 operands and
 // dk a multiple of 32.  Written as explicit stages whose LDS fragment loads are
 // issued one stage ahead of the products that use them (scheduling barriers keep
 // the compiler from sinking the loads next to their first use, which would
 // expose the LDS latency at every product).
-template <int DK, int LDK, int LDC, int LDV>
+//
+// The read-out is formed transposed, O^T = S^T (q e^G)^T + U^T (scale P)^T: the
+// MFMA operand layouts of A and B mirror each other, so the same registers serve
+// with the operands swapped, and the accumulator then holds 4 consecutive value
+// columns of one token per lane -- one 16-byte store instead of four scattered
+// ones.  Ot[r] is O[token lane & 15][wcol + 4 (lane >> 4) + r].
+// The 16-deep products (U = Tb E, P U, the state update) take their three split
+// terms in two instructions: one operand as [hi | lo] read in one piece, the
+// other's hi duplicated into both halves, so one 16x16x32 product sums two terms
+// over a lane's 8 k slots (16x16x32 costs what 16x16x16 costs on this GPU), and a
+// 16x16x16 product adds the third.
+__device__ __forceinline__ bf16x4 lo_half(const bf16x8 &x) {
+    return __builtin_shufflevector(x, x, 0, 1, 2, 3);
+}
+__device__ __forceinline__ bf16x8 twice(const bf16x4 &x) {
+    return __builtin_shufflevector(x, x, 0, 1, 2, 3, 0, 1, 2, 3);
+}
+// Row `row0 + (lane & 15)`, group lane >> 4 of an interleaved [rows][LDG] operand.
+template <int LDG>
+__device__ __forceinline__ bf16x8 ldg8(const bf16 *M, int row0, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(M + (row0 + (lane & 15)) * LDG + (lane >> 4) * 8);
+}
+
+template <int DK, int LDK, int LDG, int LDV>
 __device__ __forceinline__ void state_chain_bf16(
     f32x4 (&Sacc)[DK / 16], BReg8 (&sb)[DK / 32], f32x4 &Ot, const bf16 *sQdh, const bf16 *sQdl,
-    const bf16 *sKdh, const bf16 *sKdl, const bf16 *sKrTh, const bf16 *sKrTl, const bf16 *sTbh,
-    const bf16 *sTbl, const bf16 *sPh, const bf16 *sPl, const float *sV, const float *sEGn,
-    float scale, int wcol, int lane) {
+    const bf16 *sKdh, const bf16 *sKdl, const bf16 *sKrT, const bf16 *sTb, const bf16 *sP,
+    const float *sV, const float *sEGn, float scale, int wcol, int lane) {
     constexpr int NTK = DK / 16, NKB = DK / 32;
     static_assert(DK % 32 == 0, "shape");
     // small operands first: Tb / P fragments and V
-    const AF4 tb0 = lda4(sTbh, sTbl, LDC, 0, 0, lane), p0 = lda4(sPh, sPl, LDC, 0, 0, lane);
+    const bf16x8 tb8 = ldg8<LDG>(sTb, 0, lane), p8 = ldg8<LDG>(sP, 0, lane);
     float vin[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) vin[r] = sV[acc_row(lane, r) * LDV + wcol + (lane & 15)];
@@ -140,18 +158,18 @@ __device__ __forceinline__ void state_chain_bf16(
         __builtin_amdgcn_sched_barrier(0);
         if (j + 1 < NKB) sb[j + 1] = breg8(Sacc[2 * j + 2], Sacc[2 * j + 3]);
         Et = mma(fk[cur].h, sb[j].h, Et);
-        Ot = mma(fq[cur].h, sb[j].h, Ot);
+        Ot = mma(sb[j].h, fq[cur].h, Ot);
         Et = mma(fk[cur].h, sb[j].l, Et);
-        Ot = mma(fq[cur].h, sb[j].l, Ot);
+        Ot = mma(sb[j].l, fq[cur].h, Ot);
         Et = mma(fk[cur].l, sb[j].h, Et);
-        Ot = mma(fq[cur].l, sb[j].h, Ot);
+        Ot = mma(sb[j].h, fq[cur].l, Ot);
         __builtin_amdgcn_sched_barrier(0);
     }
     // first half of the state-update fragments load during the U and P U products
     constexpr int NK1 = NTK / 2;
-    AF4 fr4[NTK];
+    bf16x8 fr8[NTK];
 #pragma unroll
-    for (int rt = 0; rt < NK1; ++rt) fr4[rt] = lda4(sKrTh, sKrTl, LDC, rt * 16, 0, lane);
+    for (int rt = 0; rt < NK1; ++rt) fr8[rt] = ldg8<LDG>(sKrT, rt * 16, lane);
     __builtin_amdgcn_sched_barrier(0);
     // E = V - Kd S;  U = Tb E;  O = scale Qd S (the stage holds q e^G unscaled)
 #pragma unroll
@@ -160,13 +178,20 @@ __device__ __forceinline__ void state_chain_bf16(
         Ot[r] *= scale;
     }
     const BReg4 eb = breg4(Et);
-    const f32x4 Ut = mma3(tb0.h, tb0.l, eb, f32x4{0.f, 0.f, 0.f, 0.f});
+    f32x4 Ut = mma(tb8, twice(eb.h), f32x4{0.f, 0.f, 0.f, 0.f});
+    Ut = mma(lo_half(tb8), eb.l, Ut);
     const BReg4 ub4 = breg4(Ut);
-    Ot = mma3(p0.h, p0.l, ub4, Ot);
+    const bf16x8 uhh = twice(ub4.h);
+    // O^T += [U_h | U_h] [P_h | P_l]^T + U_l P_h^T, each product into fresh
+    // registers (a zero accumulator cannot overlap the running one) and added
+    const f32x4 pu1 = mma(uhh, p8, f32x4{0.f, 0.f, 0.f, 0.f});
+    const f32x4 pu2 = mma(ub4.l, lo_half(p8), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Ot[r] += pu1[r] + pu2[r];
     __builtin_amdgcn_sched_barrier(0);
     // second half of the fragments load during the first half's products
 #pragma unroll
-    for (int rt = NK1; rt < NTK; ++rt) fr4[rt] = lda4(sKrTh, sKrTl, LDC, rt * 16, 0, lane);
+    for (int rt = NK1; rt < NTK; ++rt) fr8[rt] = ldg8<LDG>(sKrT, rt * 16, lane);
     f32x4 eg[NTK];
 #pragma unroll
     for (int rt = 0; rt < NTK; ++rt)
@@ -178,11 +203,9 @@ __device__ __forceinline__ void state_chain_bf16(
 #pragma unroll
         for (int r = 0; r < 4; ++r) Sacc[rt][r] *= eg[rt][r];
 #pragma unroll
-    for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr4[rt].h, ub4.h, Sacc[rt]);
+    for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr8[rt], uhh, Sacc[rt]);
 #pragma unroll
-    for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr4[rt].h, ub4.l, Sacc[rt]);
-#pragma unroll
-    for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(fr4[rt].l, ub4.h, Sacc[rt]);
+    for (int rt = 0; rt < NTK; ++rt) Sacc[rt] = mma(lo_half(fr8[rt]), ub4.l, Sacc[rt]);
 }
 
 template <class T, class TO, int DK, int BV, int C, int GM>
@@ -256,29 +279,10 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
         };
         // Chunk bases are uniform 64-bit pointers; per-lane offsets inside a chunk
         // fit 32 bits (rows < C), which keeps the address arithmetic scalar.
-        auto load = [&](Regs &R, int64_t cs) {
+        auto load_small = [&](Regs &R, int64_t cs) {
             const int last = (int)min((int64_t)C, eos - cs) - 1;
-            const size_t bq = (size_t)cs * rowQK + (size_t)h * DK;
-            const T *qb = q + bq, *kb = k + bq;
-            const float *gb = gs.g + bq;
-            const T *zb = static_cast<const T *>(gs.z) + bq;
-            if (act) {
-#pragma unroll
-                for (int j = 0; j < RP; ++j) {
-                    const uint32_t off = (uint32_t)min(rg * RP + j, last) * (uint32_t)rowQK +
-                                         (uint32_t)(2 * cpair);
-                    R.q[j] = ld_off<T2>(qb, off * (uint32_t)sizeof(T));
-                    R.k[j] = ld_off<T2>(kb, off * (uint32_t)sizeof(T));
-                    if constexpr (GM == kGateFused)
-                        R.g[j] = ld_off<T2>(zb, off * (uint32_t)sizeof(T));
-                    else if constexpr (GM == kGateHead)
-                        R.g[j] = ld_off<float>(gs.g + (size_t)cs * H + h,
-                                               (uint32_t)min(rg * RP + j, last) * (uint32_t)H * 4u);
-                    else
-                        R.g[j] = ld_off<f32x2>(gb, off * 4u);
-                }
-            }
-            const float *tbb = tb + ((size_t)cs * H + h) * C, *pmb = pm + ((size_t)cs * H + h) * C;
+            const float *tbb = tb + ((size_t)cs * H + h) * C;
+            const float *pmb = pm + ((size_t)cs * H + h) * C;
             const uint32_t wo = ((uint32_t)min(tr, last) * (uint32_t)(H * C) + (uint32_t)tc) * 4u;
             if constexpr (NTB == 1) {
                 R.tb[0][0] = ld_off<float>(tbb, wo);
@@ -293,6 +297,34 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
             const T *vb = v + (size_t)cs * rowV + (size_t)h * DV + v0;
             R.v = ld_off<TV>(vb, ((uint32_t)min(vr, last) * (uint32_t)rowV + (uint32_t)vcol) *
                                      (uint32_t)sizeof(T));
+        };
+        auto load_row = [&](Regs &R, int64_t cs, int j) {
+            if (!act) return;
+            const int last = (int)min((int64_t)C, eos - cs) - 1;
+            const size_t bq = (size_t)cs * rowQK + (size_t)h * DK;
+            const uint32_t row = (uint32_t)min(rg * RP + j, last);
+            const uint32_t off = row * (uint32_t)rowQK + (uint32_t)(2 * cpair);
+            R.q[j] = ld_off<T2>(q + bq, off * (uint32_t)sizeof(T));
+            R.k[j] = ld_off<T2>(k + bq, off * (uint32_t)sizeof(T));
+            if constexpr (GM == kGateFused)
+                R.g[j] = ld_off<T2>(static_cast<const T *>(gs.z) + bq, off * (uint32_t)sizeof(T));
+            else if constexpr (GM == kGateHead)
+                R.g[j] = ld_off<float>(gs.g + (size_t)cs * H + h, row * (uint32_t)H * 4u);
+            else
+                R.g[j] = ld_off<f32x2>(gs.g + bq, off * 4u);
+        };
+        auto load_all = [&](Regs &R, int64_t cs) {
+            load_small(R, cs);
+#pragma unroll
+            for (int j = 0; j < RP; ++j) load_row(R, cs, j);
+        };
+
+        // Element (row, token t) of an interleaved split operand (bf16 only).
+        auto put_il = [&](T *M, int row, int t, float x) {
+            if constexpr (Cfg::kIL) {
+                T *p = M + row * Cfg::LDG + (t >> 2) * 8 + (t & 3);
+                split2(x, p[0], p[4]);
+            }
         };
 
         // Step s: build stage s & 1 from chunk s (if s < nchunks) out of `cur`, and
@@ -342,15 +374,19 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
             // are issued (vmcnt(0) here costs nothing).  Global loads and stores share
             // one in-order counter, so a wait placed after the new loads -- where the
             // compiler would put it, at the first use of `cur` -- also waits for them.
+            // The next chunk's loads are all issued here, a whole step ahead of their
+            // use (issued later, their latency shows at the next step's start).  A
+            // step without a chunk is followed only by steps without one, so it
+            // loads nothing.
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt untouched
-            if (nchunks > 0) load(nxt, bos + (int64_t)min(s + 1, nchunks - 1) * C);
+            if (!work) return;
+            load_all(nxt, bos + (int64_t)min(s + 1, nchunks - 1) * C);
             // Pin the loads here: the step barriers order LDS only, so without a
             // compiler memory barrier the loads would be sunk to their use in the
             // next step and their latency exposed there.
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            if (!work) return;
 
             char *st = smem + (s & 1) * Cfg::kStage;
             T *sQdh = reinterpret_cast<T *>(st + Cfg::oQd), *sQdl = sQdh + (SPLIT ? CKE : 0);
@@ -361,15 +397,23 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
             float *sV = reinterpret_cast<float *>(st + Cfg::oV);
             float *sEGn = reinterpret_cast<float *>(st + Cfg::oEGn);
             if (tb_act) {
-                const int i = tr * LDC + tc;
-                if constexpr (NTB == 1) {
-                    put1(sTbh, sTbl, i, tbv[0]);
-                    put1(sPh, sPl, i, pmv[0]);
-                } else {
+                if constexpr (Cfg::kIL) {
 #pragma unroll
-                    for (int e = 0; e < NTB; e += 2) {
-                        put2(sTbh, sTbl, i + e, tbv[e], tbv[e + 1]);
-                        put2(sPh, sPl, i + e, pmv[e], pmv[e + 1]);
+                    for (int e = 0; e < NTB; ++e) {
+                        put_il(sTbh, tr, tc + e, tbv[e]);
+                        put_il(sPh, tr, tc + e, pmv[e]);
+                    }
+                } else {
+                    const int i = tr * LDC + tc;
+                    if constexpr (NTB == 1) {
+                        put1(sTbh, sTbl, i, tbv[0]);
+                        put1(sPh, sPl, i, pmv[0]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < NTB; e += 2) {
+                            put2(sTbh, sTbl, i + e, tbv[e], tbv[e + 1]);
+                            put2(sPh, sPl, i + e, pmv[e], pmv[e + 1]);
+                        }
                     }
                 }
             }
@@ -414,14 +458,27 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
                 }
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const int base = (2 * cpair + e) * LDC + rg * RP;
-                    if constexpr (RP % 2 == 0) {
+                    const int ch = 2 * cpair + e;
+                    if constexpr (Cfg::kIL && RP == 4) {
+                        // the lane's 4 rows are token group rg: one 16-byte write
+                        bf16x2 h01, l01, h23, l23;
+                        split_pair(krt[e][0], krt[e][1], h01, l01);
+                        split_pair(krt[e][2], krt[e][3], h23, l23);
+                        *reinterpret_cast<u32x4 *>(sKrTh + ch * Cfg::LDG + rg * 8) =
+                            u32x4{bits(h01), bits(h23), bits(l01), bits(l23)};
+                    } else if constexpr (Cfg::kIL) {
 #pragma unroll
-                        for (int j = 0; j < RP; j += 2)
-                            put2(sKrTh, sKrTl, base + j, krt[e][j], krt[e][j + 1]);
+                        for (int j = 0; j < RP; ++j) put_il(sKrTh, ch, rg * RP + j, krt[e][j]);
                     } else {
+                        const int base = ch * LDC + rg * RP;
+                        if constexpr (RP % 2 == 0) {
 #pragma unroll
-                        for (int j = 0; j < RP; ++j) put1(sKrTh, sKrTl, base + j, krt[e][j]);
+                            for (int j = 0; j < RP; j += 2)
+                                put2(sKrTh, sKrTl, base + j, krt[e][j], krt[e][j + 1]);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < RP; ++j) put1(sKrTh, sKrTl, base + j, krt[e][j]);
+                        }
                     }
                 }
                 if (rg == 0) {
@@ -432,7 +489,7 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
         };
 
         Regs A, B;
-        if (nchunks > 0) load(A, bos);
+        if (nchunks > 0) load_all(A, bos);
         // nsteps = nchunks + 1 rounded up to even; one barrier per step
         for (int s = 0; s < nsteps; s += 2) {
             step(A, B, s);
@@ -485,23 +542,21 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
 
                 if constexpr (SPLIT && DK % 32 == 0) {
                     f32x4 Ot;
-                    state_chain_bf16<DK, LDK, LDC, LDV>(Sacc, sbs, Ot, sQdh, sQdl, sKdh, sKdl,
-                                                        sKrTh, sKrTl, sTbh, sTbl, sPh, sPl, sV,
-                                                        sEGn, scale, wave * 16, lane);
+                    state_chain_bf16<DK, LDK, Cfg::LDG, LDV>(Sacc, sbs, Ot, sQdh, sQdl, sKdh,
+                                                             sKdl, sKrTh, sTbh, sPh, sV, sEGn,
+                                                             scale, wave * 16, lane);
+                    // Ot holds token lane & 15, value columns oc .. oc + 3
                     TO *ob = o + (size_t)c0 * rowV + (size_t)h * DV;
-                    auto store = [&](bool all) {
+                    const int tok = lane & 15;
+                    const int oc = v0 + wave * 16 + (lane >> 4) * 4;
+                    if (tok < nt) {
+                        typedef TO TO4 __attribute__((ext_vector_type(4)));
+                        TO4 ov;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int row = acc_row(lane, r);
-                            if (all || row < nt)
-                                st_off<TO>(ob, ((uint32_t)row * (uint32_t)rowV + (uint32_t)vc) *
-                                                   (uint32_t)sizeof(TO),
-                                           from_f32<TO>(Ot[r]));
-                        }
-                    };
-                    // whole chunks (all but a sequence's last) store without a row test
-                    if (nt == C) store(true);
-                    else store(false);
+                        for (int r = 0; r < 4; ++r) ov[r] = from_f32<TO>(Ot[r]);
+                        st_off<TO4>(ob, ((uint32_t)tok * (uint32_t)rowV + (uint32_t)oc) *
+                                            (uint32_t)sizeof(TO), ov);
+                    }
                 } else {
                 RegB<T, NTK> Sb;
                 Sb.prepare(Sacc);

@@ -162,6 +162,20 @@ __device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// D = A B + C with D in registers disjoint from C.  Left to itself the compiler
+// may give a 16x16 product a destination that overlaps its accumulator input by
+// half a tile (D starting two registers below or above C), and the matrix unit
+// does not form the right sum for such a partial overlap; accumulating in place
+// (D and C the same registers) is fine.  Keeping C live past the product rules
+// the overlap out.  For accumulator chains whose in-place form the compiler
+// keeps on its own, plain mma() is used.
+template <class A, class B>
+__device__ __forceinline__ f32x4 mma_sep(A a, B b, f32x4 c) {
+    const f32x4 d = mma(a, b, c);
+    asm volatile("" ::"v"(c));
+    return d;
+}
+
 // k per lane for a product whose reduction length is K.
 template <class T, int K> struct KplFor { static constexpr int value = 1; };
 template <int K> struct KplFor<bf16, K> { static constexpr int value = (K % 32 == 0) ? 8 : 4; };
