@@ -17,13 +17,19 @@ constexpr bool fits() {
 }
 
 // Value-slice width.  Wave w of a state workgroup owns state columns [16w, 16w+16)
-// of its slice, so a 64-column slice keeps all four waves busy in the state
-// chain; the chunk-operand work is repeated once per slice.  64 columns when dv
-// allows, else 32, else 16.
-inline int pick_bv(int dv) {
+// of its slice; the chunk-operand work (the producers' loads and exponentials)
+// is repeated once per slice.  A workgroup's step time is set by its chain of
+// dependent chunk steps, so while the grid fits the GPU's CUs, narrower slices
+// (64 columns, one consumer wave per SIMD) finish sooner.  Once there are more
+// workgroups than CUs the work is throughput-bound: one workgroup per head with
+// all 128 columns (two consumer waves per SIMD, producers shared) then does a
+// head's work for one set of producer work.  Else 64 columns when dv allows,
+// else 32, else 16.
+inline int pick_bv(int dv, int dk, int64_t units) {
 #ifdef KDA_CHUNK_BV
     if (dv % KDA_CHUNK_BV == 0) return KDA_CHUNK_BV;
 #endif
+    if (dv == 128 && dk == 128 && units * 2 > device_cus()) return 128;
     return dv % 64 == 0 ? 64 : (dv % 32 == 0 ? 32 : 16);
 }
 
@@ -84,7 +90,10 @@ hipError_t run(const ChunkArgs &a, hipStream_t s) {
 
 template <class T, class TO, int DK, int C, int GM>
 hipError_t run_bv(const ChunkArgs &a, hipStream_t s) {
-    switch (pick_bv(a.dv)) {
+    switch (pick_bv(a.dv, DK, (int64_t)a.num_seqs * a.heads)) {
+        case 128:
+            if constexpr (DK == 128) return run<T, TO, DK, 128, C, GM>(a, s);
+            return hipErrorNotSupported;
         case 64: return run<T, TO, DK, 64, C, GM>(a, s);
         case 32: return run<T, TO, DK, 32, C, GM>(a, s);
         default: return run<T, TO, DK, 16, C, GM>(a, s);

@@ -2,15 +2,17 @@
 // chunks of each sequence with the state on chip (chunk algebra in
 // kda_chunk_common.cuh; Tb and scale * P come from the prep kernel).
 //
-// Work decomposition.  One workgroup of 8 waves owns one (sequence, head, value
-// slice of BV columns) and runs two pipelines that meet at one barrier per step:
+// Work decomposition.  One workgroup owns one (sequence, head, value slice of BV
+// columns: 64, or all 128 when there are more workgroups than CUs) and runs two
+// pipelines that meet at one barrier per step:
 //  * consumer waves 0 .. BV/16-1: wave w owns the 16 state columns [16w, 16w+16)
 //    of the slice.  Its part of the fp32 state lives in MFMA accumulator
 //    registers for the whole sequence, and the state-dependent chain of a chunk
 //    (E = V - Kd S, U = Tb E, O = Qd S + P U, the state update) runs inside that
 //    wave from registers -- an accumulator tile doubles as the B operand of the
 //    next product when the A fragment is read with the matching k order.
-//  * producer waves 4..7 build the next chunk's operands in the other half of a
+//  * the producer waves after them (4 of them) build the next chunk's operands
+//    in the other half of a
 //    double-buffered LDS stage: q e^{G}, k e^{G} and (k e^{G_n - G})^T
 //    (all factors <= 1, exponentiated directly), the split Tb and P rows, V and
 //    e^{G_n}.  A producer lane owns two key channels of a group of rows; the
@@ -38,8 +40,11 @@ struct StateCfg {
     // consumer waves + producers
     static_assert(C == 16, "chunks are 16 tokens");
     static constexpr int NPW = DK >= 64 ? KDA_STATE_NPW : 4;
-    static constexpr int NT = (4 + NPW) * kWave;
     static constexpr int NTC = C / 16, NTK = DK / 16, NCW = BV / 16;
+    // consumer wave slots (waves 0 .. NCS-1; slices narrower than 64 columns leave
+    // some idle), then the producers
+    static constexpr int NCS = NCW > 4 ? NCW : 4;
+    static constexpr int NT = (NCS + NPW) * kWave;
     // Row pitch padding (elements).  For bf16 the pitches come out at 2 (mod 32)
     // dwords, so the 16 rows one LDS cycle serves fall in 16 different bank pairs
     // (an 8-element pad would map rows r and r + 8 to the same banks); fragments are
@@ -57,7 +62,7 @@ struct StateCfg {
     // only the first C*C (C*BV) / NTB (NVE) threads take part
     static constexpr int NTB = C * C / NPT > 0 ? C * C / NPT : 1;
     static constexpr int NVE = C * BV / NPT > 0 ? C * BV / NPT : 1;
-    static_assert(CPW >= 1 && RG * RP == C && NCW <= 4 && BV % 16 == 0, "shape");
+    static_assert(CPW >= 1 && RG * RP == C && NCW <= 8 && BV % 16 == 0, "shape");
     static_assert(NTB >= 1 && (NTB == 1 || NTB % 4 == 0) && NVE >= 1, "shape");
 
     // bf16 with dk a multiple of 32 (the register-B chain below): the 16-deep
@@ -247,10 +252,10 @@ void chunk_state_kernel(const T *__restrict__ q, const T *__restrict__ k, const 
     const int v0 = slice * BV;
     const size_t rowQK = (size_t)H * DK, rowV = (size_t)H * DV;
 
-    if (wave >= 4) {
+    if (wave >= Cfg::NCS) {
         // =============================== producers ===============================
-        const int pt = tid - 4 * kWave;                       // 0 .. 255
-        const int pw = wave - 4;
+        const int pt = tid - Cfg::NCS * kWave;                // 0 .. 255
+        const int pw = wave - Cfg::NCS;
         const int cpair = pw * CPW + (lane % CPW);            // channels 2cpair, 2cpair+1
         float gc1 = 0.f, gc2a = 0.f, gc2b = 0.f, glb = 0.f;   // fused gate constants
         if constexpr (GM == kGateFused) {

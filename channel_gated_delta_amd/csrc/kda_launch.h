@@ -1,6 +1,8 @@
 // kda_launch.h -- internal launchers behind the C ABI (host code; not exported).
 #pragma once
 
+#include <atomic>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -58,6 +60,23 @@ inline size_t chunk_workspace_bytes(int64_t total_tokens, int32_t heads, int c) 
 constexpr size_t kScratchBytes = ((size_t)64 << 20) + kOrderBytes;
 constexpr int kScratchMaxDevices = 64;
 hipError_t scratch_address(void **ptr);
+
+// Compute units of the current device, looked up once per device (the layout
+// choice of the chunk kernels depends on it; both layouts give the same results,
+// so a failed lookup falls back to 256, the count of gfx950's MI355X).
+inline int device_cus() {
+    static std::atomic<int> cache[kScratchMaxDevices];   // 0: not looked up yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchMaxDevices) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 struct NormGateArgs {
     const void *o, *gate;

@@ -124,6 +124,19 @@ def test_many_packed_sequences(nseq):
     check_prefill(spec_of(lengths, H=2, h0=0.05, seed=nseq))
 
 
+WIDE_LENGTHS = [1, 3, 15, 16, 17, 31, 33, 63, 64, 65, 130, 7, 0, 40, 200] * 5   # 75 sequences
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_wide_slices_many_units(dtype):
+    """More (sequence, head) units than half the CUs: the state kernel takes all 128
+    value columns of a head in one workgroup (8 consumer waves) instead of two
+    64-column slices.  Ragged lengths, an empty sequence, h0."""
+    assert len(WIDE_LENGTHS) * 2 * 2 > torch.cuda.get_device_properties(0).multi_processor_count
+    note("wide slices: %d sequences x 2 heads %s" % (len(WIDE_LENGTHS), dtype))
+    check_prefill(spec_of(WIDE_LENGTHS, H=2, dtype=dtype, h0=0.05, seed=75))
+
+
 def test_zero_tokens():
     spec = spec_of([0], H=2, h0=0.05, seed=7)
     inp = workloads.make_prefill(spec, DEV)
@@ -201,6 +214,12 @@ def test_gated_strong_decay_and_prologue(dtype):
                         h0=0.05, seed=33))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_gated_wide_slices(dtype):
+    """The fused gate in the 128-column workgroups (many units)."""
+    check_gated(spec_of(WIDE_LENGTHS, H=2, dtype=dtype, h0=0.05, seed=76))
+
+
 def test_gated_matches_plain_gate():
     """The fused path equals chunk_fwd fed with the same gate precomputed (fp32)."""
     spec = spec_of([150, 66], H=2, h0=0.05, seed=34)
@@ -246,6 +265,12 @@ def test_gdn_chunk(dk, dv, dtype):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
 def test_gdn_strong_decay(dtype):
     check_gdn(spec_of([300, 41], H=3, dtype=dtype, lb=-8.0, gate_std=2.0, h0=0.05, seed=43))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_gdn_wide_slices(dtype):
+    """One decay per (token, head) in the 128-column workgroups (many units)."""
+    check_gdn(spec_of(WIDE_LENGTHS, H=2, dtype=dtype, h0=0.05, seed=77))
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
