@@ -193,7 +193,14 @@ def decode_step_bytes(B: int, H: int, dk: int, dv: int) -> float:
     return float(B * H * (2 * dk * dv * 4 + 2 * dk * 2 + dv * 2 + 4 * dk + 4 + 4 * dv))
 
 
-def run_prefill(args, torch, kda, workloads, gated=False, gdn=False, workload=None, steps=None):
+def run_prefill(args, torch, kda, workloads, gated=False, gdn=False, workload=None, steps=None,
+                overlap=False):
+    """Time the prefill step (3 conv calls + the chunk call) on one workload.
+
+    With ``overlap`` (plain g only) the step runs the v conv on a second stream
+    beside the q and k convs and the chunk call's prep (kda_chunk_fwd_phases: the
+    prep does not read v), and the walk waits for it; the chunk call's own time is
+    then not separable, so ``chunk_ms`` is only meaningful without overlap."""
     specs = workloads.standard_specs()
     spec = specs[workload or args.workload]
     nsteps = steps or args.steps
@@ -212,8 +219,29 @@ def run_prefill(args, torch, kda, workloads, gated=False, gdn=False, workload=No
     ws = torch.empty(kda.chunk_workspace_bytes(T, H, DK, DV, spec.chunk, spec.dtype),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream() if overlap else None
+    chunk_kw = dict(cu_seqlens=cu, scale=spec.read_scale, gate_lower_bound=spec.gate_lb,
+                    chunk_size=spec.chunk, initial_state=inp["h0"], out=ob, final_state=hT,
+                    workspace=ws)
+
+    def step_overlap(ev=None):
+        side.wait_stream(stream)          # the previous step's walk reads vb
+        with torch.cuda.stream(side):
+            kda.short_conv(inp["v_raw"], inp["w_v"], num_heads=H, head_dim=DV, cu_seqlens=cu,
+                           out=vb)
+            v_done = torch.cuda.Event()
+            v_done.record(side)
+        kda.short_conv(inp["q_raw"], inp["w_q"], num_heads=H, head_dim=DK, cu_seqlens=cu,
+                       l2_normalize=True, out=qb)
+        kda.short_conv(inp["k_raw"], inp["w_k"], num_heads=H, head_dim=DK, cu_seqlens=cu,
+                       l2_normalize=True, out=kb)
+        kda.chunk_fwd(qb, kb, vb, inp["g"], inp["beta"], **chunk_kw, phases=kda.PHASE_PREP)
+        stream.wait_event(v_done)
+        kda.chunk_fwd(qb, kb, vb, inp["g"], inp["beta"], **chunk_kw, phases=kda.PHASE_WALK)
 
     def step(ev=None):
+        if overlap:
+            return step_overlap(ev)
         kda.short_conv(inp["q_raw"], inp["w_q"], num_heads=H, head_dim=DK, cu_seqlens=cu,
                        l2_normalize=True, out=qb)
         kda.short_conv(inp["k_raw"], inp["w_k"], num_heads=H, head_dim=DK, cu_seqlens=cu,
@@ -227,10 +255,7 @@ def run_prefill(args, torch, kda, workloads, gated=False, gdn=False, workload=No
                               chunk_size=spec.chunk, initial_state=inp["h0"], out=ob,
                               final_state=hT, workspace=ws)
         elif gate is None:
-            kda.chunk_fwd(qb, kb, vb, inp["g"], inp["beta"], cu_seqlens=cu,
-                          scale=spec.read_scale, gate_lower_bound=spec.gate_lb,
-                          chunk_size=spec.chunk, initial_state=inp["h0"], out=ob, final_state=hT,
-                          workspace=ws)
+            kda.chunk_fwd(qb, kb, vb, inp["g"], inp["beta"], **chunk_kw)
         else:
             kda.chunk_fwd_gated(qb, kb, vb, gate["z"], inp["beta"], a_log=gate["a_log"],
                                 dt_bias=gate["dt_bias"], lower_bound=spec.gate_lb, cu_seqlens=cu,
@@ -253,7 +278,7 @@ def run_prefill(args, torch, kda, workloads, gated=False, gdn=False, workload=No
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    chunk_ms = sum(a.elapsed_time(b) for a, b in events) / nsteps
+    chunk_ms = None if overlap else sum(a.elapsed_time(b) for a, b in events) / nsteps
     ms_step = total_ms / nsteps
     return dict(spec=spec, T=T, N=N, ms_step=ms_step, chunk_ms=chunk_ms, inp=inp, o=ob,
                 steps=nsteps)
@@ -384,16 +409,19 @@ def spec_key(spec) -> str:
 
 
 def sub_line(args, torch, kda, workloads, name, steps):
-    """The prefill step on another workload: tokens/s and the chunk call's roofline."""
+    """The prefill step on another workload: tokens/s (the v conv beside the chunk prep,
+    as in the main line) and the chunk call's roofline (timed in the one-stream step)."""
     res = run_prefill(args, torch, kda, workloads, workload=name, steps=steps)
+    ores = run_prefill(args, torch, kda, workloads, workload=name, steps=steps, overlap=True)
     spec = res["spec"]
-    out = {"workload": spec.name, "value": round(res["T"] / (res["ms_step"] / 1e3), 1),
+    out = {"workload": spec.name, "value": round(res["T"] / (ores["ms_step"] / 1e3), 1),
            "unit": "tokens/s", "tokens": res["T"], "sequences": res["N"],
-           "ms_per_step": round(res["ms_step"], 4), "steps": res["steps"],
+           "ms_per_step": round(ores["ms_step"], 4),
+           "serial_ms_per_step": round(res["ms_step"], 4), "steps": res["steps"],
            "chunk_tokens_per_s": round(res["T"] / (res["chunk_ms"] / 1e3), 1),
            "roofline": chunk_roofline(spec, res, "kda_chunk_fwd (chunk_prep16_kernel + "
                                       "chunk_state_kernel)", prefill_step_bytes, "chunk")}
-    del res
+    del res, ores
     torch.cuda.empty_cache()
     return out
 
@@ -434,23 +462,27 @@ def main():
         copy_calibration(torch)
         return
 
-    res = run_prefill(args, torch, kda, workloads)
+    res = run_prefill(args, torch, kda, workloads)                 # the chunk call's own time
+    ores = run_prefill(args, torch, kda, workloads, overlap=True)  # the step as it runs best
     spec = res["spec"]
     H, DK, DV, T, N = spec.heads, spec.dk, spec.dv, res["T"], res["N"]
-    tok_s = T / (res["ms_step"] / 1e3)
+    tok_s = T / (ores["ms_step"] / 1e3)
     roof = chunk_roofline(spec, res, "kda_chunk_fwd (chunk_prep16_kernel + chunk_state_kernel)",
                           prefill_step_bytes, "chunk")
     useful = prefill_useful_flops(T, H, DK, DV, spec.chunk)
     ut = useful / (res["chunk_ms"] / 1e3) / 1e12
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_step"], 4),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ores["ms_step"], 4),
+        "serial_ms_per_step": round(res["ms_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; no weights or datasets)",
         "config": {"workload": spec.name, "batch": N, "seq_len": T, "heads": H, "dk": DK,
                    "dv": DV, "chunk_requested": spec.chunk, "chunk_internal": 16,
-                   "path": "3x short_conv (conv4+SiLU, q/k L2) + chunk_fwd (fp32 o)"},
+                   "path": "3x short_conv (conv4+SiLU, q/k L2) + chunk_fwd (fp32 o); the v "
+                           "conv on a second stream beside the q/k convs and the chunk prep "
+                           "(kda_chunk_fwd_phases), the walk after both"},
         "roofline": roof,
         "mfma": {"useful_gflop_per_launch": round(useful / 1e9, 2),
                  "useful_tflops": round(ut, 1), "peak_tflops": 2500.0,
@@ -522,7 +554,7 @@ def main():
                          "unit": "GB/s", "frac": round(each / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("epilogue", args.workload),
                          "kernel": "norm_gate_kernel", "algorithmic_bytes_per_launch": ebytes}}
-    out["prologue_ms_per_step"] = round(out["ms_per_step"] - roof["avg_launch_ms"], 4)
+    out["prologue_ms_per_step"] = round(out["serial_ms_per_step"] - roof["avg_launch_ms"], 4)
     out["prologue_bytes_per_step"] = prologue_bytes(T, H, DK)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(keep_res, workloads)

@@ -31,6 +31,7 @@ __all__ = ["KdaError", "library", "short_conv", "chunk_fwd", "chunk_fwd_gated", 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP, KDA_ERR_WORKSPACE = 0, 1, 2, 3, 4
+PHASE_PREP, PHASE_WALK, PHASE_ALL = 1, 2, 3   # kda_chunk_fwd_phases
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 _lib = None
@@ -70,6 +71,7 @@ def library() -> ctypes.CDLL:
         lib.kda_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
                                         _vp, _i32, _i32, _vp]
         lib.kda_gdn_chunk_fwd.argtypes = lib.kda_chunk_fwd.argtypes
+        lib.kda_chunk_fwd_phases.argtypes = lib.kda_chunk_fwd.argtypes[:-1] + [_i32, _vp]
         lib.kda_chunk_fwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32,
                                               _i32, _i32, _f32, _f32, _vp, _vp, _vp, _i32, _i32,
                                               _vp]
@@ -77,7 +79,7 @@ def library() -> ctypes.CDLL:
         for fn in ("kda_short_conv", "kda_chunk_fwd", "kda_chunk_fwd_gated",
                    "kda_chunk_fwd_workspace_size", "kda_decode_step", "kda_output_norm_gate",
                    "kda_decode_step_conv", "kda_gdn_chunk_fwd", "kda_gdn_decode_step",
-                   "kda_chunk_fwd_noalloc"):
+                   "kda_chunk_fwd_noalloc", "kda_chunk_fwd_phases"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_status_string.restype = ctypes.c_char_p
@@ -170,18 +172,22 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               scale: Optional[float] = None, gate_lower_bound: float = -5.0, chunk_size: int = 64,
               initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
               out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-              out_dtype: torch.dtype = torch.float32, workspace: Optional[torch.Tensor] = None
-              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              out_dtype: torch.dtype = torch.float32, workspace: Optional[torch.Tensor] = None,
+              phases: int = 3) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise KDA prefill.  q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H].
 
     Returns o [T, H, dv] (``out_dtype``, fp32 by default) and the final states
     [N, H, dk, dv] (fp32) if requested.  ``workspace`` (a uint8 GPU tensor of at
     least ``chunk_workspace_bytes(...)`` bytes) is allocated when not given.
+    ``phases`` (kda_chunk_fwd_phases): PHASE_PREP enqueues the prep only (into
+    ``workspace``, which the caller then passes to the PHASE_WALK call with the
+    same arguments), PHASE_WALK the walk only, PHASE_ALL both.
     """
     T, H, dk = q.shape
     _dev(g, "g", torch.float32, (T, H, dk))
     return _chunk(q, k, v, g, None, beta, cu_seqlens, scale, gate_lower_bound, chunk_size,
-                  initial_state, output_final_state, out, final_state, out_dtype, workspace)
+                  initial_state, output_final_state, out, final_state, out_dtype, workspace,
+                  phases)
 
 
 def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
@@ -261,7 +267,7 @@ def chunk_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, z: torch.
 
 
 def _chunk(q, k, v, g, gate, beta, cu_seqlens, scale, lower_bound, chunk_size, initial_state,
-           output_final_state, out, final_state, out_dtype, workspace):
+           output_final_state, out, final_state, out_dtype, workspace, phases=3):
     _dev(q, "q")
     dt = q.dtype
     if dt not in _DTYPES:
@@ -289,7 +295,13 @@ def _chunk(q, k, v, g, gate, beta, cu_seqlens, scale, lower_bound, chunk_size, i
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace", torch.uint8)
-    if gate is None or gate == "head":
+    if gate is None and phases != PHASE_ALL:
+        _check(library().kda_chunk_fwd_phases(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,
+            int(chunk_size), sc, float(lower_bound), _ptr(initial_state), _ptr(final_state),
+            _ptr(o), _ptr(workspace), workspace.numel(), _DTYPES[dt], _DTYPES[out_dtype],
+            int(phases), _stream(q)))
+    elif gate is None or gate == "head":
         fn = library().kda_chunk_fwd if gate is None else library().kda_gdn_chunk_fwd
         _check(fn(
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,

@@ -254,6 +254,26 @@ KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, 
                                 stream);
 }
 
+KDA_API kda_status_t kda_chunk_fwd_phases(const void *q, const void *k, const void *v,
+                                          const float *g, const float *beta,
+                                          const int32_t *cu_seqlens, int32_t num_seqs,
+                                          int64_t total_tokens, int32_t num_heads, int32_t dk,
+                                          int32_t dv, int32_t chunk_size, float scale,
+                                          float gate_lower_bound, const float *initial_state,
+                                          float *final_state, void *o, void *workspace,
+                                          size_t workspace_bytes, kda_dtype_t dtype,
+                                          kda_dtype_t out_dtype, int32_t phases, void *stream) {
+    g_last_error[0] = '\0';
+    if (phases != KDA_PHASE_PREP && phases != KDA_PHASE_WALK && phases != KDA_PHASE_ALL)
+        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd_phases: phases %d not 1, 2 or 3", phases);
+    kda::ChunkArgs a{q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, dk,
+                     dv, chunk_size, scale, gate_lower_bound, initial_state, final_state, o,
+                     (float *)workspace, nullptr, nullptr, nullptr};
+    a.phases = phases;
+    return chunk_checked_launch("kda_chunk_fwd_phases", a, g, 0, workspace_bytes, dtype,
+                                out_dtype, stream);
+}
+
 KDA_API kda_status_t kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
                                            const float *g, const float *beta,
                                            const int32_t *cu_seqlens, int32_t num_seqs,

@@ -49,15 +49,16 @@ hipError_t run(const ChunkArgs &a, hipStream_t s) {
         const GateSrc gs{a.g, a.gz, a.a_log, a.dt_bias, a.gate_lb};
         float *pm = tb ? tb + (size_t)a.total_tokens * a.heads * C : nullptr;
         int32_t *order = nullptr;
-        if (a.total_tokens > 0 && a.cu_seqlens && a.num_seqs > 1 && a.num_seqs <= kOrderMaxSeqs) {
+        if (a.total_tokens > 0 && a.cu_seqlens && a.num_seqs > 1 && a.num_seqs <= kOrderMaxSeqs)
             order = reinterpret_cast<int32_t *>(pm + (size_t)a.total_tokens * a.heads * C);
+        if (order && (a.phases & 1)) {
             hipLaunchKernelGGL(seq_order_kernel<kOrderMaxSeqs>,
                                dim3((unsigned)((a.num_seqs + 255) / 256)),
                                dim3(256), 0, s, a.cu_seqlens, a.num_seqs, a.total_tokens, order);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        if (a.total_tokens > 0) {
+        if (a.total_tokens > 0 && (a.phases & 1)) {
             const int64_t ntiles = (a.total_tokens + C - 1) / C;
             if constexpr (std::is_same<T, bf16>::value && DK % 32 == 0) {
                 // one wave per (tile, head), four per workgroup
@@ -75,6 +76,7 @@ hipError_t run(const ChunkArgs &a, hipStream_t s) {
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
+        if (!(a.phases & 2)) return hipSuccess;
         // The state kernel also runs without tokens: it writes h0 (or zeros) to hT.
         const int units = a.num_seqs * a.heads;
         const int nslice = a.dv / BV;

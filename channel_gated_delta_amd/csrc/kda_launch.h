@@ -37,6 +37,9 @@ struct ChunkArgs {
     // activation dtype, A_log [H] and dt_bias [H, dk] (NULL = 0); gate_lb is its bound
     const void *gz;
     const float *a_log, *dt_bias;
+    // which launches to enqueue: 1 the prep (a packed batch's walking order, then
+    // Tb / P into the workspace), 2 the walk over the chunks, 3 both
+    int32_t phases = 3;
 };
 
 // Packed batches of up to kOrderMaxSeqs sequences run their longest sequences

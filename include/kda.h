@@ -170,6 +170,40 @@ KDA_API kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, 
                            kda_dtype_t out_dtype, void *stream);
 
 /*
+ * kda_chunk_fwd_phases -- kda_chunk_fwd in two separately enqueued parts, so that
+ * the first can overlap independent work on another stream (for instance the
+ * convolution of v, which it does not read).
+ *
+ *   phases = KDA_PHASE_PREP: the prep only -- a packed batch's walking order and,
+ *            for every chunk and head, Tb and scale * P -- into the workspace.  It
+ *            reads q, k, g, beta and cu_seqlens; it does not touch v,
+ *            initial_state, final_state or o.
+ *   phases = KDA_PHASE_WALK: the walk over the chunks only.  It reads the workspace
+ *            as left by a PREP call with the same arguments, which the caller must
+ *            order before it (same stream, or an event between streams), and
+ *            writes o and final_state.
+ *   phases = KDA_PHASE_ALL:  both, exactly kda_chunk_fwd.
+ * PREP then WALK gives results bit-identical to kda_chunk_fwd.  Every other
+ * argument, the workspace size, the supported shapes and the errors are those of
+ * kda_chunk_fwd (both parts check all of them, v and o included); a phases
+ * value other than these three is KDA_ERR_INVALID_ARG.
+ */
+enum {
+    KDA_PHASE_PREP = 1,
+    KDA_PHASE_WALK = 2,
+    KDA_PHASE_ALL = 3
+};
+KDA_API kda_status_t kda_chunk_fwd_phases(const void *q, const void *k, const void *v,
+                                          const float *g, const float *beta,
+                                          const int32_t *cu_seqlens, int32_t num_seqs,
+                                          int64_t total_tokens, int32_t num_heads, int32_t dk,
+                                          int32_t dv, int32_t chunk_size, float scale,
+                                          float gate_lower_bound, const float *initial_state,
+                                          float *final_state, void *o, void *workspace,
+                                          size_t workspace_bytes, kda_dtype_t dtype,
+                                          kda_dtype_t out_dtype, int32_t phases, void *stream);
+
+/*
  * kda_chunk_fwd_noalloc -- kda_chunk_fwd for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): the same computation and arguments without the workspace.

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
                           "kda_chunk_fwd_workspace_size", "kda_decode_step",
                           "kda_output_norm_gate", "kda_decode_step_conv", "kda_gdn_chunk_fwd",
                           "kda_gdn_decode_step", "kda_status_string", "kda_last_error",
-                          "kda_version", "kda_chunk_fwd_noalloc"}
+                          "kda_version", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_phases"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -64,6 +64,37 @@ def chunk(lib, **kw):
     return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"], a["T"],
                              a["H"], a["dk"], a["dv"], a["chunk"], a["scale"], a["lb"], a["h0"],
                              a["hT"], a["o"], a["ws"], a["wsb"], a["dtype"], a["odt"], NULL)
+
+
+def phased(lib, phases, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, cu=NULL, N=1, T=64, H=2, dk=128, dv=128, chunk=64,
+             scale=0.1, lb=-5.0, h0=NULL, hT=NULL, o=ctypes.c_void_p(8192),
+             ws=ctypes.c_void_p(1 << 20), wsb=1 << 30, dtype=BF16, odt=F32)
+    a.update(kw)
+    return lib.kda_chunk_fwd_phases(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"],
+                                    a["T"], a["H"], a["dk"], a["dv"], a["chunk"], a["scale"],
+                                    a["lb"], a["h0"], a["hT"], a["o"], a["ws"], a["wsb"],
+                                    a["dtype"], a["odt"], phases, NULL)
+
+
+@pytest.mark.parametrize("phases", [0, 4, -1, 7])
+def test_chunk_fwd_phases_rejects_unknown_phases(lib, phases):
+    assert phased(lib, phases) == kda.KDA_ERR_INVALID_ARG
+    assert b"phases" in lib.kda_last_error()
+
+
+@pytest.mark.parametrize("phases", [kda.PHASE_PREP, kda.PHASE_WALK, kda.PHASE_ALL])
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), kda.KDA_ERR_INVALID_ARG),
+    (dict(o=P), kda.KDA_ERR_INVALID_ARG),
+    (dict(dk=48), kda.KDA_ERR_UNSUPPORTED),
+    (dict(ws=NULL), kda.KDA_ERR_WORKSPACE),
+    (dict(wsb=2 * 64 * 2 * 16 * 4 + 4096 - 1), kda.KDA_ERR_WORKSPACE),
+])
+def test_chunk_fwd_phases_checks_every_argument(lib, phases, kw, status):
+    """Each part runs the full argument checks of kda_chunk_fwd (host only)."""
+    assert phased(lib, phases, **kw) == status
+    assert lib.kda_last_error()
 
 
 def ws_size(lib, T=64, H=2, dk=128, dv=128, chunk=64, dtype=BF16, odt=F32):

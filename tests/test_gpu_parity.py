@@ -137,6 +137,37 @@ def test_wide_slices_many_units(dtype):
     check_prefill(spec_of(WIDE_LENGTHS, H=2, dtype=dtype, h0=0.05, seed=75))
 
 
+@pytest.mark.parametrize("lengths", [[4096], RAGGED], ids=["one", "packed"])
+def test_phases_prep_then_walk_bitwise(lengths):
+    """kda_chunk_fwd_phases: the prep on one stream, the walk on another after an
+    event, gives o and final states bit-identical to the one-call kda_chunk_fwd;
+    the prep alone writes neither o nor the final state (both stay NaN)."""
+    spec = spec_of(lengths, H=3, h0=0.05, seed=len(lengths))
+    inp = workloads.make_prefill(spec, DEV)
+    ref = gpu_prefill(inp, spec)
+    check_written(ref)
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+    kw = dict(cu_seqlens=inp["cu_seqlens"], scale=spec.read_scale, initial_state=inp["h0"])
+    T, H = spec.total_tokens, spec.heads
+    ws = torch.full((kda.chunk_workspace_bytes(T, H, 128, 128, 64, torch.bfloat16,
+                                               torch.float32),), 0xFF, dtype=torch.uint8,
+                    device=DEV)
+    o = torch.full((T, H, 128), float("nan"), device=DEV)
+    hT = torch.full((len(lengths), H, 128, 128), float("nan"), device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kda.chunk_fwd(*args, **kw, out=o, final_state=hT, workspace=ws, phases=kda.PHASE_PREP)
+        done = torch.cuda.Event()
+        done.record(side)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(o).all()) and bool(torch.isnan(hT).all())
+    torch.cuda.current_stream().wait_event(done)
+    kda.chunk_fwd(*args, **kw, out=o, final_state=hT, workspace=ws, phases=kda.PHASE_WALK)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref["o"]) and torch.equal(hT, ref["hT"])
+
+
 def test_zero_tokens():
     spec = spec_of([0], H=2, h0=0.05, seed=7)
     inp = workloads.make_prefill(spec, DEV)
