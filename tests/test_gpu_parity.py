@@ -79,9 +79,11 @@ def test_strong_decay(lb, std, dtype):
                           dtype=dtype))
 
 
-def test_bf16_output_is_rounded_fp32_output():
-    """With bf16 inputs, a bf16 o is exactly the fp32 o rounded to nearest even."""
-    spec = spec_of([130, 64], H=2, h0=0.05, seed=21)
+@pytest.mark.parametrize("lengths", [[130, 64], [130, 64] * 40], ids=["narrow", "wide"])
+def test_bf16_output_is_rounded_fp32_output(lengths):
+    """With bf16 inputs, a bf16 o is exactly the fp32 o rounded to nearest even (also
+    in the 128-column workgroups: 80 sequences x 2 heads)."""
+    spec = spec_of(lengths, H=2, h0=0.05, seed=21)
     inp = workloads.make_prefill(spec, DEV)
     o32, h32 = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
                              cu_seqlens=inp["cu_seqlens"], initial_state=inp["h0"])
