@@ -68,13 +68,22 @@ KERNEL_SOURCES = {
 }
 
 
+def code_text(src: str) -> str:
+    """C/C++ source without comments and with whitespace runs collapsed: what the
+    compiler sees, so that editing a comment does not date a counter summary."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_digest(kind: str) -> str:
-    """Hash of the sources a kernel is built from (to date counter summaries)."""
+    """Hash of the code (comments and layout excluded) of the sources a kernel is built
+    from, to date counter summaries."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "channel_gated_delta_amd", "csrc")
     for name in KERNEL_SOURCES[kind]:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -36,8 +36,8 @@ struct StateCfg {
     static constexpr int DK = DK_, BV = BV_, C = C_;
     static constexpr bool kSplit = std::is_same<T, bf16>::value;
     static constexpr int NSPLIT = kSplit ? 2 : 1;
-    // producer waves (KDA_STATE_NPW for dk >= 64 and 16-token chunks), threads: 4
-    // consumer waves + producers
+    // producer waves (KDA_STATE_NPW for dk >= 64 and 16-token chunks); threads: NCS
+    // consumer wave slots, then the producers
     static_assert(C == 16, "chunks are 16 tokens");
     static constexpr int NPW = DK >= 64 ? KDA_STATE_NPW : 4;
     static constexpr int NTC = C / 16, NTK = DK / 16, NCW = BV / 16;
